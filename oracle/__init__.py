@@ -1,0 +1,216 @@
+"""CPU oracle for block-scaled microscaling quantization.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+library (``fp8_quantize_pack_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``mxq_oracle.c`` (plain scalar C, one element at a
+time, in the order the source pages state each step; see the header of that
+file for the citations and the readings of open points).  This module builds it
+with gcc and marshals torch CPU tensors to it; it does no arithmetic itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxq_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle_mxq.so")
+
+CFLAGS = ["-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off",
+          "-fexcess-precision=standard", "-fPIC", "-shared"]
+
+_DT = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+_FMT = {"fp8": 0, "mxfp4": 1, "nvfp4": 2}
+_MODE = {"row": 0, "given": 1, "tensor": 2}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle into ``liboracle_mxq.so`` (always recompiles)."""
+    tmp = LIB_PATH + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if (not os.path.exists(LIB_PATH)
+                or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.orc_e2m1_decode.restype = ctypes.c_double
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint32]
+        L.orc_e2m1_round_mag.restype = ctypes.c_uint32
+        L.orc_e2m1_round_mag.argtypes = [ctypes.c_float]
+        L.orc_round_binary.restype = ctypes.c_double
+        L.orc_round_binary.argtypes = [ctypes.c_double, i32, i32]
+        L.orc_e4m3_decode.restype = ctypes.c_double
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint32]
+        L.orc_e4m3_encode.restype = ctypes.c_uint32
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_e8m0_decode.restype = ctypes.c_double
+        L.orc_e8m0_decode.argtypes = [ctypes.c_uint32]
+        L.orc_pow2_ceil.restype = ctypes.c_float
+        L.orc_pow2_ceil.argtypes = [ctypes.c_float]
+        L.orc_floor_log2.restype = i32
+        L.orc_floor_log2.argtypes = [ctypes.c_float]
+        L.orc_quantize_mxfp4.restype = None
+        L.orc_quantize_mxfp4.argtypes = [vp, i32, i64, i64, vp, vp]
+        L.orc_dequantize_mxfp4.restype = None
+        L.orc_dequantize_mxfp4.argtypes = [vp, vp, i64, i64, vp, i32]
+        L.orc_quantize_nvfp4.restype = None
+        L.orc_quantize_nvfp4.argtypes = [vp, i32, i64, i64, i32, vp, i64,
+                                         vp, vp, vp]
+        L.orc_dequantize_nvfp4.restype = None
+        L.orc_dequantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, vp, i32]
+        L.orc_quantize_cache.restype = None
+        L.orc_quantize_cache.argtypes = [vp, vp, i32, i64, i64, i32, i64]
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- helpers
+
+def _cpu(t: torch.Tensor) -> torch.Tensor:
+    if t.device.type != "cpu":
+        raise ValueError("the oracle takes CPU tensors")
+    return t.contiguous()
+
+
+def _rows(shape, K):
+    n = 1
+    for s in shape[:-1]:
+        n *= s
+    return n
+
+
+# ---------------------------------------------------------------- primitives
+
+def e2m1_decode(code: int) -> float:
+    return lib().orc_e2m1_decode(code)
+
+
+def e2m1_round_mag(q: float) -> int:
+    return lib().orc_e2m1_round_mag(q)
+
+
+def round_binary(v: float, p: int, emin: int) -> float:
+    return lib().orc_round_binary(v, p, emin)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(v)
+
+
+def e4m3_decode(b: int) -> float:
+    return lib().orc_e4m3_decode(b)
+
+
+def e8m0_decode(b: int) -> float:
+    return lib().orc_e8m0_decode(b)
+
+
+def pow2_ceil(v: float) -> float:
+    return lib().orc_pow2_ceil(v)
+
+
+def floor_log2(a: float) -> int:
+    return lib().orc_floor_log2(a)
+
+
+# ---------------------------------------------------------------- operations
+
+def quantize_mxfp4(x: torch.Tensor):
+    """[..., K] -> (uint8 packed [..., K//2], uint8 e8m0 scale bytes [..., K//32])."""
+    x = _cpu(x)
+    K = x.shape[-1]
+    assert K % 32 == 0
+    R = _rows(x.shape, K)
+    packed = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8)
+    scales = torch.empty(*x.shape[:-1], K // 32, dtype=torch.uint8)
+    lib().orc_quantize_mxfp4(x.data_ptr(), _DT[x.dtype], R, K,
+                             packed.data_ptr(), scales.data_ptr())
+    return packed, scales
+
+
+def dequantize_mxfp4(packed: torch.Tensor, scales: torch.Tensor,
+                     dtype: torch.dtype) -> torch.Tensor:
+    packed, scales = _cpu(packed), _cpu(scales)
+    K = packed.shape[-1] * 2
+    R = _rows(packed.shape, K)
+    y = torch.empty(*packed.shape[:-1], K, dtype=dtype)
+    lib().orc_dequantize_mxfp4(packed.data_ptr(), scales.data_ptr(), R, K,
+                               y.data_ptr(), _DT[dtype])
+    return y
+
+
+def quantize_nvfp4(x: torch.Tensor, mode: str = "row",
+                   given: torch.Tensor | None = None):
+    """[..., K] -> (uint8 packed [..., K//2], uint8 e4m3 bytes [..., K//16],
+    float32 row scales [...]).  mode: 'row' | 'given' | 'tensor'."""
+    x = _cpu(x)
+    K = x.shape[-1]
+    assert K % 16 == 0
+    R = _rows(x.shape, K)
+    packed = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8)
+    scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8)
+    row_scale = torch.empty(*x.shape[:-1], dtype=torch.float32)
+    gptr, gstride = None, 0
+    if mode == "given":
+        given = _cpu(given.to(torch.float32))
+        if given.numel() == 1:
+            gstride = 0
+        else:
+            assert given.numel() == R
+            gstride = 1
+        gptr = given.data_ptr()
+    lib().orc_quantize_nvfp4(x.data_ptr(), _DT[x.dtype], R, K, _MODE[mode],
+                             gptr, gstride, packed.data_ptr(),
+                             scales.data_ptr(), row_scale.data_ptr())
+    return packed, scales, row_scale
+
+
+def dequantize_nvfp4(packed: torch.Tensor, scales: torch.Tensor,
+                     row_scale: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    packed, scales = _cpu(packed), _cpu(scales)
+    row_scale = _cpu(row_scale.to(torch.float32))
+    K = packed.shape[-1] * 2
+    R = _rows(packed.shape, K)
+    assert row_scale.numel() == R
+    y = torch.empty(*packed.shape[:-1], K, dtype=dtype)
+    lib().orc_dequantize_nvfp4(packed.data_ptr(), scales.data_ptr(),
+                               row_scale.data_ptr(), R, K, y.data_ptr(),
+                               _DT[dtype])
+    return y
+
+
+def quantize_cache(x: torch.Tensor, fmt: str, block_size: int) -> torch.Tensor:
+    """Quantize/dequantize round trip; same shape and dtype as x."""
+    x = _cpu(x)
+    C = x.shape[-1]
+    R = _rows(x.shape, C)
+    y = torch.empty_like(x)
+    lib().orc_quantize_cache(x.data_ptr(), y.data_ptr(), _DT[x.dtype], R, C,
+                             _FMT[fmt], block_size)
+    return y
+
+
+def store_values(v: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    """Round float32 values to dtype through the oracle's store routine."""
+    v = _cpu(v.to(torch.float32)).reshape(-1)
+    L = lib()
+    L.orc_store.restype = None
+    L.orc_store.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float]
+    y = torch.empty(v.numel(), dtype=dtype)
+    for i in range(v.numel()):
+        L.orc_store(y.data_ptr(), _DT[dtype], i, float(v[i]))
+    return y

@@ -1,0 +1,427 @@
+/*
+ * mxq_oracle.c -- plain, slow, scalar CPU oracle for block-scaled microscaling
+ * quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the bench may build, load or call this file.  The GPU
+ * library shares no code, header, table or helper with it.
+ *
+ * Build: gcc -std=c11 -O2 -fno-fast-math -ffp-contract=off -fPIC -shared
+ * (x86-64 SSE arithmetic: binary32 ops are IEEE round-to-nearest-even with
+ * subnormals kept).  Every "RN" below is one such binary32 operation.
+ *
+ * Sources, cited by page title and section:
+ *  [mxfp4 page]  "nemo_automodel.components.quantization.mxfp4":
+ *                quantize_mxfp4, dequantize_mxfp4, Data (_FP4_E2M1_TABLE,
+ *                _FP4_E2M1_MIDPOINTS, _FP4_BYTE_TABLE, MXFP4_BLOCK_SIZE).
+ *  [nvfp4 page]  "nemo_automodel.components.quantization.nvfp4":
+ *                module introduction, quantize_nvfp4, quantize_nvfp4_modelopt,
+ *                dequantize_nvfp4, _check_last_dim, Data (E2M1_MAX, E4M3_MAX,
+ *                E4M3_MIN_SUBNORMAL, NVFP4_BLOCK_SIZE).
+ *  [cache page]  "nemo_automodel.components.models.deepseek_v41.quantization":
+ *                quantize_cache, _power_of_two_ceiling, _CacheQuantization.
+ *  [modelopt]    Model-Optimizer tensor_quantizer.py: TensorQuantizer.forward
+ *                (inputs upcast to float before quantizing; blocks padded with
+ *                zeros), _FP8_E4M3_MIN_POSITIVE (scale clamp).
+ *
+ * Readings where the pages are silent, ambiguous or cut off:
+ *  R1 midpoint ties go to the smaller magnitude (a count of midpoints strictly
+ *     below |q|, i.e. the lower bucket of the midpoint table);
+ *  R2 the sign nibble is the sign bit of the input, also when |q| rounds to 0;
+ *  R3 floor(log2(amax)) is exact (taken from the binary exponent);
+ *  R4 an MXFP4 scale below 2^-127 is stored as byte 0 and the block is
+ *     quantized with that stored scale; amax = 0 gives byte 0;
+ *  R5 NVFP4 arithmetic is binary32, evaluated left to right as the formula is
+ *     written: g = A / 2688, u = (a / 6) / g, den = sigma * g, q = x / den;
+ *  R6 NVFP4 block scales are clamped to [2^-9, 448] before the e4m3 cast
+ *     (maxNum: a NaN ratio takes the lower bound);
+ *  R9 cache scales: fp8 and mxfp4 use the power-of-two ceiling of
+ *     amax / elem_max (elem_max 448 or 6), floored at the smallest normal
+ *     binary32; nvfp4 uses a single e4m3 scale e4m3(clamp(amax / 6));
+ *  R10 a partial last cache group behaves as if zero-padded;
+ *  R11 the fp8 cache keeps the sign of zero; e2m1 codes decode through the
+ *     table, whose index 8 holds +0.0;
+ *  R14 e4m3 encodes saturate at 448.
+ */
+#include "mxq_oracle.h"
+
+#include <float.h>
+#include <math.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------
+ * Number formats
+ * ---------------------------------------------------------------------- */
+
+/* The e2m1 value table, [mxfp4 page] Data, _FP4_E2M1_TABLE: 16 entries, the
+ * first eight are the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; entry 8 is +0.0
+ * and entries 9..15 are the negatives of entries 1..7 (the printed list is
+ * cut off after -2; the rest follows by sign symmetry and E2M1_MAX = 6 on the
+ * [nvfp4 page] Data section). */
+static const double E2M1_TABLE[16] = {
+    0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+    0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0};
+
+/* The rounding midpoints, [mxfp4 page] Data, _FP4_E2M1_MIDPOINTS (float32). */
+static const float E2M1_MIDPOINTS[7] = {0.25f, 0.75f, 1.25f, 1.75f,
+                                        2.5f,  3.5f,  5.0f};
+
+double orc_e2m1_decode(uint32_t code) { return E2M1_TABLE[code & 15u]; }
+
+/* Round a scaled value to an e2m1 magnitude index: the number of midpoints
+ * that lie strictly below |q| (reading R1: a value on a midpoint takes the
+ * lower bucket).  NaN compares false everywhere and gives 0; values beyond
+ * the last midpoint give 7, i.e. saturate at 6. */
+uint32_t orc_e2m1_round_mag(float q) {
+  float a = fabsf(q);
+  uint32_t n = 0;
+  for (int j = 0; j < 7; ++j)
+    if (a > E2M1_MIDPOINTS[j]) ++n;
+  return n;
+}
+
+/* e2m1 code of element x whose scaled value is q (reading R2). */
+static uint32_t e2m1_code(float x, float q) {
+  return (signbit(x) ? 8u : 0u) | orc_e2m1_round_mag(q);
+}
+
+/* Round v to the nearest number with a p-bit significand (implicit bit
+ * included) and exponent >= emin (smaller magnitudes use the subnormal
+ * quantum 2^(emin-p+1)); no upper exponent bound; ties to even.
+ * This is the textbook definition of round-to-nearest-even into a binary
+ * floating-point format; callers apply their own overflow rule. */
+double orc_round_binary(double v, int p, int emin) {
+  if (v == 0.0 || isnan(v) || isinf(v)) return v;
+  double a = fabs(v);
+  int ex;
+  (void)frexp(a, &ex); /* a = m * 2^ex, m in [0.5, 1): floor(log2 a) = ex-1 */
+  int e = ex - 1;
+  if (e < emin) e = emin;
+  double quantum = ldexp(1.0, e - (p - 1));
+  double n = a / quantum;       /* exact: scaling by a power of two */
+  double r = nearbyint(n) * quantum; /* default rounding: to nearest even */
+  return v < 0 ? -r : r;
+}
+
+/* float8 e4m3fn decoding (bias 7, 3 mantissa bits, subnormal quantum 2^-9,
+ * no infinities, 0x7F/0xFF are NaN).  The [nvfp4 page] names the dtype and
+ * its constants E4M3_MAX = 448 and E4M3_MIN_SUBNORMAL = 2^-9. */
+double orc_e4m3_decode(uint32_t byte) {
+  byte &= 0xFFu;
+  int s = (byte >> 7) & 1, E = (byte >> 3) & 15, m = byte & 7;
+  if (E == 15 && m == 7) return NAN;
+  double v = (E == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, E - 7);
+  return s ? -v : v;
+}
+
+/* float8 e4m3fn encoding of v: round to nearest even on the e4m3 grid
+ * (4-bit significand, minimum exponent -6), saturating at 448 (reading R14),
+ * then write the byte whose decoding is that value.  The sign bit is kept. */
+uint32_t orc_e4m3_encode(float v) {
+  double r = orc_round_binary(fabs((double)v), 4, -6);
+  if (r > 448.0) r = 448.0;
+  uint32_t byte;
+  if (r < ldexp(1.0, -6)) {
+    byte = (uint32_t)(r / ldexp(1.0, -9)); /* subnormal: m * 2^-9 */
+  } else {
+    int ex;
+    double m = frexp(r, &ex); /* r = m * 2^ex, m in [0.5, 1) */
+    int E = ex - 1;           /* r = (1 + f/8) * 2^E */
+    uint32_t f = (uint32_t)((m * 2.0 - 1.0) * 8.0);
+    byte = ((uint32_t)(E + 7) << 3) | f;
+  }
+  return (signbit(v) ? 0x80u : 0u) | byte;
+}
+
+/* float8 e8m0fnu decoding: 2^(b-127); 0xFF is NaN ([mxfp4 page] names the
+ * dtype float8_e8m0fnu for the block scales). */
+double orc_e8m0_decode(uint32_t byte) {
+  byte &= 0xFFu;
+  if (byte == 0xFFu) return NAN;
+  return ldexp(1.0, (int)byte - 127);
+}
+
+/* floor(log2(a)) for a > 0, exact (reading R3). */
+int orc_floor_log2(float a) {
+  int ex;
+  (void)frexpf(a, &ex);
+  return ex - 1;
+}
+
+/* [cache page] _power_of_two_ceiling: the smallest power of two that is >= v,
+ * for a positive normal binary32 v. */
+float orc_pow2_ceil(float v) {
+  int ex;
+  float m = frexpf(v, &ex); /* v = m * 2^ex, m in [0.5, 1) */
+  if (m == 0.5f) return v;  /* already a power of two */
+  return ldexpf(1.0f, ex);
+}
+
+/* ---- element load / store for the three floating dtypes ---- */
+
+static float f16_bits_to_float(uint16_t h) {
+  int s = (h >> 15) & 1, E = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (E == 31) v = m ? NAN : INFINITY;
+  else if (E == 0) v = ldexp((double)m, -24);
+  else v = ldexp(1.0 + m / 1024.0, E - 15);
+  return (float)(s ? -v : v);
+}
+
+float orc_load(const void* x, int dtype, int64_t i) {
+  if (dtype == 0) return ((const float*)x)[i];
+  uint16_t h = ((const uint16_t*)x)[i];
+  if (dtype == 1) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+  }
+  return f16_bits_to_float(h);
+}
+
+/* Round a binary32 value to the output dtype: round-to-nearest-even, IEEE
+ * overflow to infinity. */
+void orc_store(void* y, int dtype, int64_t i, float v) {
+  if (dtype == 0) { ((float*)y)[i] = v; return; }
+  uint16_t out;
+  if (isnan(v)) {
+    out = (dtype == 1) ? 0x7FC0u : 0x7E00u;
+  } else if (dtype == 1) {
+    /* bfloat16: 8-bit significand, same exponent range as binary32 */
+    double r = orc_round_binary((double)v, 8, -126);
+    double maxv = ldexp(2.0 - ldexp(1.0, -7), 127);
+    if (fabs(r) > maxv) r = signbit(v) ? -INFINITY : INFINITY;
+    float rf = (float)r; /* exact: r is a bfloat16 value */
+    uint32_t u;
+    memcpy(&u, &rf, 4);
+    out = (uint16_t)(u >> 16);
+  } else {
+    /* float16: 11-bit significand, exponents -14..15 */
+    double r = orc_round_binary((double)v, 11, -14);
+    uint16_t s = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(r);
+    if (a > 65504.0) out = s | 0x7C00u;
+    else if (a == 0.0) out = s;
+    else if (a < ldexp(1.0, -14)) out = s | (uint16_t)(a / ldexp(1.0, -24));
+    else {
+      int ex;
+      double m = frexp(a, &ex); /* a = m * 2^ex, m in [0.5,1) */
+      int E = ex - 1;
+      uint16_t man = (uint16_t)((m * 2.0 - 1.0) * 1024.0);
+      out = s | (uint16_t)((E + 15) << 10) | man;
+    }
+  }
+  ((uint16_t*)y)[i] = out;
+}
+
+/* ------------------------------------------------------------------------
+ * MXFP4  ([mxfp4 page] quantize_mxfp4, dequantize_mxfp4)
+ * ---------------------------------------------------------------------- */
+
+#define MXFP4_BLOCK 32 /* [mxfp4 page] Data, MXFP4_BLOCK_SIZE */
+
+/* Quantize along the last dim: one e8m0 scale per 32 columns, the scale being
+ * 2^(floor(log2(amax)) - 2) ([mxfp4 page] quantize_mxfp4), two e2m1 codes per
+ * byte with the even column in the low nibble ([mxfp4 page] introduction). */
+void orc_quantize_mxfp4(const void* x, int dtype, int64_t rows, int64_t K,
+                        uint8_t* packed, uint8_t* scales) {
+  int64_t nblk = K / MXFP4_BLOCK;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nblk; ++b) {
+      int64_t base = r * K + b * MXFP4_BLOCK;
+      /* step 1: block amax */
+      float amax = 0.0f;
+      for (int j = 0; j < MXFP4_BLOCK; ++j) {
+        float v = fabsf(orc_load(x, dtype, base + j));
+        if (v > amax) amax = v;
+      }
+      /* step 2: scale exponent floor(log2 amax) - 2, stored as e8m0 (R4) */
+      int e = (amax > 0.0f) ? orc_floor_log2(amax) - 2 : -127;
+      if (e < -127) e = -127;
+      uint8_t sbyte = (uint8_t)(e + 127);
+      scales[r * nblk + b] = sbyte;
+      float scale = (float)orc_e8m0_decode(sbyte);
+      /* step 3: divide by the scale, round to e2m1, pack pairs */
+      uint32_t code[MXFP4_BLOCK];
+      for (int j = 0; j < MXFP4_BLOCK; ++j) {
+        float v = orc_load(x, dtype, base + j);
+        code[j] = e2m1_code(v, v / scale);
+      }
+      for (int j = 0; j < MXFP4_BLOCK; j += 2)
+        packed[(base + j) / 2] = (uint8_t)(code[j] | (code[j + 1] << 4));
+    }
+  }
+}
+
+/* Decode: unpack the two nibbles (low nibble = even column), look up the e2m1
+ * table, multiply by the e8m0 scale 2^(b-127) in binary32, round to dtype
+ * ([mxfp4 page] dequantize_mxfp4 and _FP4_BYTE_TABLE). */
+void orc_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scales,
+                          int64_t rows, int64_t K, void* y, int dtype) {
+  int64_t nblk = K / MXFP4_BLOCK;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t i = r * K + k;
+      uint8_t byte = packed[i / 2];
+      uint32_t code = (k & 1) ? (byte >> 4) : (byte & 15u);
+      float scale = (float)orc_e8m0_decode(scales[r * nblk + k / MXFP4_BLOCK]);
+      float v = (float)orc_e2m1_decode(code) * scale;
+      orc_store(y, dtype, i, v);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * NVFP4  ([nvfp4 page] quantize_nvfp4, quantize_nvfp4_modelopt,
+ *         dequantize_nvfp4, Data)
+ * ---------------------------------------------------------------------- */
+
+#define NVFP4_BLOCK 16           /* NVFP4_BLOCK_SIZE */
+static const float E2M1_MAX = 6.0f;   /* E2M1_MAX */
+static const float E4M3_MAX = 448.0f; /* E4M3_MAX */
+#define E4M3_MIN_SUBNORMAL 0.001953125f /* 2^-9, E4M3_MIN_SUBNORMAL */
+
+/* Block-scale clamp (reading R6): maxNum with the smallest e4m3 subnormal
+ * (fmaxf returns the non-NaN operand), then min with E4M3_MAX. */
+static float clamp_block_scale(float u) {
+  return fminf(fmaxf(u, E4M3_MIN_SUBNORMAL), E4M3_MAX);
+}
+
+/* Quantize along the last dim ([nvfp4 page] quantize_nvfp4):
+ *   global      = amax / (6 * 448)                (per row, or given)
+ *   block_scale = e4m3(amax(block) / 6 / global)
+ *   code        = round_to_e2m1(w / (block_scale * global))
+ * mode 2 uses one amax for the whole tensor ([nvfp4 page]
+ * quantize_nvfp4_modelopt) and writes that one scale to every row. */
+void orc_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t K,
+                        int mode, const float* given, int64_t given_stride,
+                        uint8_t* packed, uint8_t* scales, float* row_scale) {
+  int64_t nblk = K / NVFP4_BLOCK;
+  float tensor_amax = 0.0f;
+  if (mode == 2) {
+    for (int64_t i = 0; i < rows * K; ++i) {
+      float v = fabsf(orc_load(x, dtype, i));
+      if (v > tensor_amax) tensor_amax = v;
+    }
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    /* step 1: the row's global scale */
+    float g;
+    if (mode == 1) {
+      g = given[r * given_stride];
+    } else {
+      float amax = tensor_amax;
+      if (mode == 0) {
+        amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+          float v = fabsf(orc_load(x, dtype, r * K + k));
+          if (v > amax) amax = v;
+        }
+      }
+      g = amax / (E2M1_MAX * E4M3_MAX); /* 6 * 448 = 2688, exact */
+    }
+    row_scale[r] = g;
+    for (int64_t b = 0; b < nblk; ++b) {
+      int64_t base = r * K + b * NVFP4_BLOCK;
+      /* step 2: block amax and the e4m3 block scale */
+      float a = 0.0f;
+      for (int j = 0; j < NVFP4_BLOCK; ++j) {
+        float v = fabsf(orc_load(x, dtype, base + j));
+        if (v > a) a = v;
+      }
+      float u = a / E2M1_MAX;
+      u = u / g;
+      uint32_t sbyte = orc_e4m3_encode(clamp_block_scale(u));
+      scales[r * nblk + b] = (uint8_t)sbyte;
+      float sigma = (float)orc_e4m3_decode(sbyte);
+      /* step 3: divide by block_scale * global, round to e2m1, pack */
+      float den = sigma * g;
+      uint32_t code[NVFP4_BLOCK];
+      for (int j = 0; j < NVFP4_BLOCK; ++j) {
+        float v = orc_load(x, dtype, base + j);
+        code[j] = e2m1_code(v, v / den);
+      }
+      for (int j = 0; j < NVFP4_BLOCK; j += 2)
+        packed[(base + j) / 2] = (uint8_t)(code[j] | (code[j + 1] << 4));
+    }
+  }
+}
+
+/* Decode ([nvfp4 page] dequantize_nvfp4): e2m1 * float(e4m3 block scale) *
+ * row scale, binary32 intermediates evaluated left to right, one final
+ * rounding to dtype. */
+void orc_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales,
+                          const float* row_scale, int64_t rows, int64_t K,
+                          void* y, int dtype) {
+  int64_t nblk = K / NVFP4_BLOCK;
+  for (int64_t r = 0; r < rows; ++r) {
+    float g = row_scale[r];
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t i = r * K + k;
+      uint8_t byte = packed[i / 2];
+      uint32_t code = (k & 1) ? (byte >> 4) : (byte & 15u);
+      float sigma = (float)orc_e4m3_decode(scales[r * nblk + k / NVFP4_BLOCK]);
+      float t = (float)orc_e2m1_decode(code) * sigma;
+      float z = t * g;
+      orc_store(y, dtype, i, z);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Cache quantize/dequantize round trip ([cache page] quantize_cache,
+ * _CacheQuantization.forward, _power_of_two_ceiling)
+ * ---------------------------------------------------------------------- */
+
+/* One group of n <= block_size consecutive channels (n < block_size only for
+ * the last group of a row, which then behaves as if zero-padded: the padding
+ * never raises the amax and is never written, reading R10). */
+static void cache_group(const void* x, void* y, int dtype, int64_t base,
+                        int64_t n, int fmt) {
+  float a = 0.0f;
+  for (int64_t j = 0; j < n; ++j) {
+    float v = fabsf(orc_load(x, dtype, base + j));
+    if (v > a) a = v;
+  }
+  if (fmt == 0) {
+    /* fp8: power-of-two scale >= amax / 448, values stored as e4m3 */
+    float v = fmaxf(a / E4M3_MAX, FLT_MIN);
+    float s = orc_pow2_ceil(v);
+    for (int64_t j = 0; j < n; ++j) {
+      float xv = orc_load(x, dtype, base + j);
+      uint32_t qb = orc_e4m3_encode(xv / s); /* sign kept (R11) */
+      float out = (float)orc_e4m3_decode(qb) * s;
+      orc_store(y, dtype, base + j, out);
+    }
+  } else if (fmt == 1) {
+    /* mxfp4: power-of-two (e8m0) scale >= amax / 6, values e2m1 */
+    float v = fmaxf(a / E2M1_MAX, FLT_MIN);
+    float s = orc_pow2_ceil(v);
+    for (int64_t j = 0; j < n; ++j) {
+      float xv = orc_load(x, dtype, base + j);
+      uint32_t c = e2m1_code(xv, xv / s);
+      float out = (float)orc_e2m1_decode(c) * s;
+      orc_store(y, dtype, base + j, out);
+    }
+  } else {
+    /* nvfp4: one e4m3 scale per group, values e2m1 */
+    float sigma =
+        (float)orc_e4m3_decode(orc_e4m3_encode(clamp_block_scale(a / E2M1_MAX)));
+    for (int64_t j = 0; j < n; ++j) {
+      float xv = orc_load(x, dtype, base + j);
+      uint32_t c = e2m1_code(xv, xv / sigma);
+      float out = (float)orc_e2m1_decode(c) * sigma;
+      orc_store(y, dtype, base + j, out);
+    }
+  }
+}
+
+void orc_quantize_cache(const void* x, void* y, int dtype, int64_t rows,
+                        int64_t C, int fmt, int64_t block_size) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c0 = 0; c0 < C; c0 += block_size) {
+      int64_t n = (C - c0 < block_size) ? C - c0 : block_size;
+      cache_group(x, y, dtype, r * C + c0, n, fmt);
+    }
+}

@@ -1,0 +1,54 @@
+/*
+ * mxq_oracle.h -- plain, slow CPU oracle for block-scaled microscaling
+ * quantization (MXFP4, NVFP4, block-scaled cache QDQ).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This header and mxq_oracle.c are used by the
+ * test-suite, by the smoke check and by the CPU-baseline leg of the bench.
+ * The product library never includes, links or calls anything here, and this
+ * oracle shares no code, table or helper with the GPU path.
+ *
+ * All data pointers are host pointers to contiguous row-major arrays.
+ * Element dtypes: 0 = float32, 1 = bfloat16 (raw 16-bit patterns),
+ * 2 = float16 (raw 16-bit patterns).
+ */
+#ifndef MXQ_ORACLE_H
+#define MXQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- primitives (exported so the tests can pin them one by one) ---- */
+double   orc_e2m1_decode(uint32_t code);            /* D(c)                        */
+uint32_t orc_e2m1_round_mag(float q);               /* R(q): 0..7                  */
+double   orc_round_binary(double v, int p, int emin); /* RN to p-bit significand */
+double   orc_e4m3_decode(uint32_t byte);
+uint32_t orc_e4m3_encode(float v);                  /* sign kept, saturates at 448 */
+double   orc_e8m0_decode(uint32_t byte);
+float    orc_pow2_ceil(float v);
+int      orc_floor_log2(float a);                   /* a > 0                       */
+float    orc_load(const void* x, int dtype, int64_t i);
+void     orc_store(void* y, int dtype, int64_t i, float v);
+
+/* ---- the five operations ---- */
+void orc_quantize_mxfp4(const void* x, int dtype, int64_t rows, int64_t K,
+                        uint8_t* packed, uint8_t* scales);
+void orc_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scales,
+                          int64_t rows, int64_t K, void* y, int dtype);
+/* mode 0: per-row amax, 1: given (given[r * given_stride]), 2: whole-tensor amax */
+void orc_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t K,
+                        int mode, const float* given, int64_t given_stride,
+                        uint8_t* packed, uint8_t* scales, float* row_scale);
+void orc_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales,
+                          const float* row_scale, int64_t rows, int64_t K,
+                          void* y, int dtype);
+/* fmt 0: fp8 (e4m3 values, power-of-two scale), 1: mxfp4, 2: nvfp4 */
+void orc_quantize_cache(const void* x, void* y, int dtype, int64_t rows,
+                        int64_t C, int fmt, int64_t block_size);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
