@@ -1,0 +1,269 @@
+"""fp8_quantize_pack_amd -- block-scaled microscaling quantization on MI355X.
+
+A thin ctypes binding over ``libmxq.so`` (HIP kernels for gfx950; C ABI in
+``include/mxq.h``).  Every step of every operation runs in the library's
+kernels; this module only checks arguments, allocates outputs with
+``torch.empty`` and passes device pointers and the current stream.  There is no
+CPU fallback: importing fails if the library has not been built.
+
+Two layers, named after the C ABI and after the source pages:
+
+* ``mxq_quantize_mxfp4`` ... ``mxq_quantize_cache``: one-to-one wrappers of the
+  C calls taking preallocated torch CUDA tensors (no allocation).
+* ``quantize_mxfp4``, ``dequantize_mxfp4``, ``quantize_nvfp4``,
+  ``quantize_nvfp4_modelopt``, ``dequantize_nvfp4``, ``quantize_cache``:
+  allocate and return new tensors with the dtypes and shapes the pages give
+  ("nemo_automodel.components.quantization.mxfp4" / ".nvfp4" and
+  "nemo_automodel.components.models.deepseek_v41.quantization").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxq.so")
+
+MXQ_F32, MXQ_BF16, MXQ_F16 = 0, 1, 2
+FORMATS = {"fp8": 0, "mxfp4": 1, "nvfp4": 2}
+NV_MODES = {"row": 0, "given": 1, "tensor": 2}
+_DT = {torch.float32: MXQ_F32, torch.bfloat16: MXQ_BF16, torch.float16: MXQ_F16}
+
+MXFP4_BLOCK_SIZE = 32
+NVFP4_BLOCK_SIZE = 16
+
+_STATUS = {
+    0: "MXQ_OK", 1: "MXQ_E_NULL", 2: "MXQ_E_SHAPE", 3: "MXQ_E_DTYPE",
+    4: "MXQ_E_FORMAT", 5: "MXQ_E_BLOCK", 6: "MXQ_E_SIZE", 7: "MXQ_E_LAUNCH",
+    8: "MXQ_E_MODE", 9: "MXQ_E_ALIGN",
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m fp8_quantize_pack_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.mxq_quantize_mxfp4.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    L.mxq_dequantize_mxfp4.argtypes = [vp, vp, i64, i64, vp, i32, vp]
+    L.mxq_quantize_nvfp4.argtypes = [vp, i32, i64, i64, i32, vp, i64, vp, vp, vp, vp, vp]
+    L.mxq_dequantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, vp, i32, vp]
+    L.mxq_quantize_cache.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp]
+    for f in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
+              "mxq_dequantize_nvfp4", "mxq_quantize_cache"):
+        getattr(L, f).restype = ctypes.c_int
+    L.mxq_status_string.argtypes = [ctypes.c_int]
+    L.mxq_status_string.restype = ctypes.c_char_p
+    L.mxq_abi_version.argtypes = []
+    L.mxq_abi_version.restype = ctypes.c_int32
+    return L
+
+
+lib = _load()
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        msg = lib.mxq_status_string(status).decode()
+        super().__init__(f"{call}: {_STATUS.get(status, status)} ({msg})")
+
+
+def _check(status: int, call: str) -> None:
+    if status == 0:
+        return
+    if status == 2:
+        raise ValueError(str(MxqError(status, call)))
+    if status == 3:
+        raise TypeError(str(MxqError(status, call)))
+    raise MxqError(status, call)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream=None):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dt(t_dtype) -> int:
+    if t_dtype not in _DT:
+        raise TypeError(f"unsupported floating dtype {t_dtype}")
+    return _DT[t_dtype]
+
+
+def _rows(t: torch.Tensor) -> int:
+    k = t.shape[-1] if t.dim() else 1
+    return t.numel() // k if k else 0
+
+
+def _dev_input(t: torch.Tensor) -> torch.Tensor:
+    """Contiguous and 16-byte aligned (copies only when it has to)."""
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    t = t.contiguous()
+    if t.data_ptr() % 16:
+        t = t.clone()
+    return t
+
+
+# ------------------------------------------------------------------ C ABI layer
+
+def mxq_quantize_mxfp4(x, packed, scales, stream=None) -> None:
+    K = x.shape[-1]
+    _check(lib.mxq_quantize_mxfp4(_ptr(x), _dt(x.dtype), _rows(x), K,
+                                  _ptr(packed), _ptr(scales), _stream(x, stream)),
+           "mxq_quantize_mxfp4")
+
+
+def mxq_dequantize_mxfp4(packed, scales, y, stream=None) -> None:
+    K = y.shape[-1]
+    _check(lib.mxq_dequantize_mxfp4(_ptr(packed), _ptr(scales), _rows(y), K,
+                                    _ptr(y), _dt(y.dtype), _stream(y, stream)),
+           "mxq_dequantize_mxfp4")
+
+
+def mxq_quantize_nvfp4(x, packed, scales, row_scale, mode="row", given=None,
+                       given_stride=1, scratch=None, stream=None) -> None:
+    K = x.shape[-1]
+    _check(lib.mxq_quantize_nvfp4(_ptr(x), _dt(x.dtype), _rows(x), K,
+                                  NV_MODES[mode], _ptr(given), given_stride,
+                                  _ptr(scratch), _ptr(packed), _ptr(scales),
+                                  _ptr(row_scale), _stream(x, stream)),
+           "mxq_quantize_nvfp4")
+
+
+def mxq_dequantize_nvfp4(packed, scales, row_scale, y, stream=None) -> None:
+    K = y.shape[-1]
+    _check(lib.mxq_dequantize_nvfp4(_ptr(packed), _ptr(scales), _ptr(row_scale),
+                                    _rows(y), K, _ptr(y), _dt(y.dtype),
+                                    _stream(y, stream)),
+           "mxq_dequantize_nvfp4")
+
+
+def mxq_quantize_cache(x, y, fmt, block_size, stream=None) -> None:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown cache format {fmt!r}; expected one of {list(FORMATS)}")
+    C = x.shape[-1] if x.dim() else 1
+    _check(lib.mxq_quantize_cache(_ptr(x), _ptr(y), _dt(x.dtype), _rows(x), C,
+                                  FORMATS[fmt], int(block_size), _stream(x, stream)),
+           "mxq_quantize_cache")
+
+
+# ------------------------------------------------------------------ tensor API
+
+def quantize_mxfp4(weight: torch.Tensor):
+    """[..., K] (K % 32 == 0) -> (int8 packed [..., K//2],
+    float8_e8m0fnu scales [..., K//32])."""
+    K = weight.shape[-1]
+    if K % MXFP4_BLOCK_SIZE:
+        raise ValueError(f"last dim {K} is not divisible by {MXFP4_BLOCK_SIZE}")
+    x = _dev_input(weight)
+    packed = torch.empty(*x.shape[:-1], K // 2, dtype=torch.int8, device=x.device)
+    scales = torch.empty(*x.shape[:-1], K // 32, dtype=torch.uint8, device=x.device)
+    mxq_quantize_mxfp4(x, packed, scales)
+    return packed, scales.view(torch.float8_e8m0fnu)
+
+
+def dequantize_mxfp4(packed: torch.Tensor, scales: torch.Tensor,
+                     dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """(int8 [..., K//2], e8m0 [..., K//32]) -> [..., K] in dtype."""
+    p = _dev_input(packed.view(torch.int8))
+    s = _dev_input(scales.view(torch.uint8))
+    K = p.shape[-1] * 2
+    if K % MXFP4_BLOCK_SIZE or s.shape[-1] != K // MXFP4_BLOCK_SIZE:
+        raise ValueError("packed/scales shapes do not describe 32-column blocks")
+    y = torch.empty(*p.shape[:-1], K, dtype=dtype, device=p.device)
+    mxq_dequantize_mxfp4(p, s, y)
+    return y
+
+
+def _check_last_dim(k: int) -> None:
+    if k % NVFP4_BLOCK_SIZE:
+        raise ValueError(f"last dim {k} is not a whole number of "
+                         f"{NVFP4_BLOCK_SIZE}-column blocks")
+
+
+def quantize_nvfp4(weight: torch.Tensor, global_scale: torch.Tensor | None = None):
+    """[..., K] -> (uint8 packed [..., K//2], float8_e4m3fn scales [..., K//16],
+    float32 row scales [...]).  One scale per row (amax / (6 * 448)) unless
+    ``global_scale`` (broadcastable to ``weight.shape[:-1]``) is given."""
+    K = weight.shape[-1]
+    _check_last_dim(K)
+    x = _dev_input(weight)
+    lead = tuple(x.shape[:-1])
+    packed = torch.empty(*lead, K // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(*lead, K // 16, dtype=torch.uint8, device=x.device)
+    row_scale = torch.empty(lead, dtype=torch.float32, device=x.device)
+    if global_scale is None:
+        mxq_quantize_nvfp4(x, packed, scales, row_scale, mode="row")
+    else:
+        g = global_scale.to(device=x.device, dtype=torch.float32)
+        if g.numel() == 1:
+            g, stride = g.reshape(1).contiguous(), 0
+        else:
+            g, stride = g.expand(lead).contiguous(), 1
+        mxq_quantize_nvfp4(x, packed, scales, row_scale, mode="given",
+                           given=g, given_stride=stride)
+    return packed, scales.view(torch.float8_e4m3fn), row_scale
+
+
+def quantize_nvfp4_modelopt(weight: torch.Tensor):
+    """2-D [out, in] -> (uint8 [out, in//2], float8_e4m3fn [out, in//16],
+    float32 scalar tensor scale amax / (6 * 448))."""
+    if weight.dim() != 2:
+        raise ValueError("quantize_nvfp4_modelopt takes a 2-D [out, in] matrix")
+    K = weight.shape[-1]
+    _check_last_dim(K)
+    x = _dev_input(weight)
+    packed = torch.empty(x.shape[0], K // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[0], K // 16, dtype=torch.uint8, device=x.device)
+    row_scale = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    scratch = torch.empty(1, dtype=torch.float32, device=x.device)
+    mxq_quantize_nvfp4(x, packed, scales, row_scale, mode="tensor", scratch=scratch)
+    g = row_scale[0] if x.shape[0] else (scratch[0] * 0)
+    return packed, scales.view(torch.float8_e4m3fn), g
+
+
+def dequantize_nvfp4(packed: torch.Tensor, scales: torch.Tensor,
+                     global_scale: torch.Tensor,
+                     dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """(uint8/int8 [..., K//2], e4m3 [..., K//16], float32 [...]) -> [..., K]."""
+    p = _dev_input(packed.view(torch.uint8))
+    s = _dev_input(scales.view(torch.uint8))
+    K = p.shape[-1] * 2
+    _check_last_dim(K)
+    if s.shape[-1] != K // NVFP4_BLOCK_SIZE:
+        raise ValueError("scales do not describe 16-column blocks of packed")
+    g = global_scale.to(device=p.device, dtype=torch.float32)
+    g = g.expand(p.shape[:-1]).contiguous()
+    y = torch.empty(*p.shape[:-1], K, dtype=dtype, device=p.device)
+    mxq_dequantize_nvfp4(p, s, g, y)
+    return y
+
+
+def quantize_cache(values: torch.Tensor, format: str, block_size: int) -> torch.Tensor:
+    """Quantize/dequantize round trip of [..., channels] in groups of
+    ``block_size`` channels; returns a new tensor with the input's shape and
+    dtype.  format: 'fp8' | 'mxfp4' | 'nvfp4'."""
+    if format not in FORMATS:
+        raise ValueError(f"unknown cache format {format!r}")
+    if block_size < 1:
+        raise ValueError("block_size must be >= 1")
+    x = values.contiguous()
+    if x.device.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    y = torch.empty_like(x)
+    mxq_quantize_cache(x, y, format, block_size)
+    return y
+
+
+def abi_version() -> int:
+    return lib.mxq_abi_version()

@@ -1,0 +1,122 @@
+// k_mxfp4.hip -- MXFP4 quantize-pack and dequantize kernels for gfx950.
+//
+// Method: "nemo_automodel.components.quantization.mxfp4", sections
+// quantize_mxfp4 / dequantize_mxfp4 / Data.  Per 32-column block: scale
+// 2^(floor(log2 amax) - 2) stored as an e8m0 byte, elements divided by it and
+// rounded to the nearest e2m1 value (ties to the smaller magnitude), two codes
+// per byte with the even column in the low nibble.
+//
+// Layout of the work.  Blocks never straddle rows (K % 32 == 0), so the tensor
+// is a flat run of 8-element chunks.  A wavefront tile is kUnroll x 64 chunks:
+// in step u lane l owns chunk tile*512 + u*64 + l, so every vector load and
+// store instruction of the wave touches one contiguous 1 KiB (bf16 input) or
+// 256 B (packed) range, and the 4 lanes of a quad own one 32-column block
+// (their amax is combined with two DPP quad permutes).  A tile covers 128
+// blocks, so its 128 scale bytes fill one 128-byte cache line.
+#include "mxq_kernel_common.h"
+#include "mxq_launch.h"
+
+namespace mxq {
+
+constexpr int kUnroll = 8;
+constexpr int kTileChunks = kUnroll * kWave;   // 512 chunks = 4096 elements
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_mxfp4_quant(
+    const void* __restrict__ x, uint32_t* __restrict__ packed,
+    uint8_t* __restrict__ scales, int64_t nchunks, int64_t ntiles) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+       t < ntiles; t += nwaves) {
+    const int64_t c0 = t * kTileChunks + lane;
+    Raw8<DT> r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = c0 + u * kWave;
+      r[u] = (c < nchunks) ? ld8<DT>(x, c) : zero8<DT>();
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = c0 + u * kWave;
+      float f[8];
+      unpack8<DT>(r[u], f);
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+      a = group_max<4>(a);                      // amax of the 32-column block
+      const uint32_t sb = mxfp4_scale_byte(a);  // e8m0 byte
+      const uint32_t word = mxfp4_quant8(f, sb, DT == DT_F32);
+      if (c < nchunks) {
+        __builtin_nontemporal_store(word, packed + c);
+        if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_mxfp4_dequant(
+    const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+    void* __restrict__ y, int64_t nchunks, int64_t ntiles) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+       t < ntiles; t += nwaves) {
+    const int64_t c0 = t * kTileChunks + lane;
+    uint32_t w[kUnroll], sb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = c0 + u * kWave;
+      const bool ok = c < nchunks;
+      w[u] = ok ? __builtin_nontemporal_load(packed + c) : 0u;
+      sb[u] = ok ? (uint32_t)scales[c >> 2] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = c0 + u * kWave;
+      float f[8];
+      mxfp4_dequant8(w[u], sb[u], f);
+      if (c < nchunks) st8<DT>(y, c, f);
+    }
+  }
+}
+
+static int grid_for(int64_t ntiles) {
+  // Enough resident waves to cover latency on 256 CUs; the loop strides the
+  // rest.  4 waves per workgroup.
+  const int64_t max_blocks = 256 * 8;
+  int64_t b = (ntiles + 3) / 4;
+  return (int)(b < max_blocks ? (b > 0 ? b : 1) : max_blocks);
+}
+
+hipError_t launch_mxfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
+                              int8_t* packed, uint8_t* scales, hipStream_t s) {
+  const int64_t nchunks = rows * (K / 8);
+  const int64_t ntiles = (nchunks + kTileChunks - 1) / kTileChunks;
+  const dim3 grid(grid_for(ntiles)), block(256);
+  uint32_t* p = reinterpret_cast<uint32_t*>(packed);
+  switch (dt) {
+    case DT_F32: hipLaunchKernelGGL(k_mxfp4_quant<DT_F32>, grid, block, 0, s, x, p, scales, nchunks, ntiles); break;
+    case DT_BF16: hipLaunchKernelGGL(k_mxfp4_quant<DT_BF16>, grid, block, 0, s, x, p, scales, nchunks, ntiles); break;
+    default: hipLaunchKernelGGL(k_mxfp4_quant<DT_F16>, grid, block, 0, s, x, p, scales, nchunks, ntiles); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_dequant(const int8_t* packed, const uint8_t* scales,
+                                int64_t rows, int64_t K, void* y, int dt,
+                                hipStream_t s) {
+  const int64_t nchunks = rows * (K / 8);
+  const int64_t ntiles = (nchunks + kTileChunks - 1) / kTileChunks;
+  const dim3 grid(grid_for(ntiles)), block(256);
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
+  switch (dt) {
+    case DT_F32: hipLaunchKernelGGL(k_mxfp4_dequant<DT_F32>, grid, block, 0, s, p, scales, y, nchunks, ntiles); break;
+    case DT_BF16: hipLaunchKernelGGL(k_mxfp4_dequant<DT_BF16>, grid, block, 0, s, p, scales, y, nchunks, ntiles); break;
+    default: hipLaunchKernelGGL(k_mxfp4_dequant<DT_F16>, grid, block, 0, s, p, scales, y, nchunks, ntiles); break;
+  }
+  return hipGetLastError();
+}
+
+} // namespace mxq

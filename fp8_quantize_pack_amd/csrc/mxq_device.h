@@ -1,0 +1,299 @@
+// mxq_device.h -- per-element arithmetic and wave primitives for the gfx950
+// kernels of libmxq.
+//
+// The element math (MXQ_HD functions) is written so that it also compiles for
+// the host: the test-suite builds it into a small host library and checks it
+// exhaustively against the CPU oracle without a GPU.  Everything here is plain
+// binary32/binary64 IEEE arithmetic plus integer bit manipulation; no fast-math
+// and no contraction (the library is compiled with -ffp-contract=off, and the
+// only fused multiply-adds are the explicit fmaf/fma calls below).
+//
+// Formats (sources cited by page title and section):
+//  e2m1: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6, rounding midpoints .25 .. 5
+//        ("nemo_automodel.components.quantization.mxfp4", Data section);
+//        a value on a midpoint rounds to the smaller magnitude.
+//  e8m0: 2^(b - 127) (same page, scales of quantize_mxfp4).
+//  e4m3fn: bias 7, 3 mantissa bits, max 448, subnormal quantum 2^-9
+//        ("nemo_automodel.components.quantization.nvfp4", Data section).
+#pragma once
+
+#include <stdint.h>
+#include <string.h>
+
+#if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define MXQ_HD __host__ __device__ __forceinline__
+#else
+#include <math.h>
+#define MXQ_HD static inline
+#endif
+
+namespace mxq {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum : int { FMT_FP8 = 0, FMT_MXFP4 = 1, FMT_NVFP4 = 2 };
+
+MXQ_HD uint32_t fbits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+MXQ_HD float bitsf(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+MXQ_HD int32_t imin(int32_t a, int32_t b) { return a < b ? a : b; }
+MXQ_HD int32_t imax(int32_t a, int32_t b) { return a > b ? a : b; }
+
+// ---------------------------------------------------------------- e2m1
+
+// Rounding constants for the bit-level e2m1 rounding.  For q in [1, 8) the
+// float32 pattern of q, plus (2^21 - 1), shifted right by 22, is 252 + code:
+// the kept mantissa bit is bit 22 and the +(2^21 - 1) rounds a remainder that
+// is strictly above one half up and a remainder of exactly one half down,
+// which is "ties to the smaller magnitude" because the e2m1 midpoints above 1
+// (1.25, 1.75, 2.5, 3.5, 5) are exactly the half-way points of that grid.
+constexpr int32_t kHiBias = 0x1FFFFF - (252 << 22);
+// For q in [0, 1) the e2m1 grid is 0, 0.5, 1 with midpoints 0.25 and 0.75;
+// 1 + q lies in [1, 2) whose 1-bit-mantissa grid is 1, 1.5, 2 with the same
+// relative midpoints, so the same rounding applied to 1 + q gives 254 + code.
+constexpr int32_t kLoBias = 0x1FFFFF - (254 << 22);
+constexpr int32_t kCodeMax = 7 << 22;
+
+// Magnitude code (0..7) of q = a * s, where a = |x| has at most 12
+// significant bits (a bfloat16 or float16 input) and s is a power of two.
+// Exactness: a * s is exact; 1 + q is exact whenever q >= 2^-13 (its lowest
+// set bit is then >= 2^-23), and for smaller q both 1 + q and the result are
+// below 1.25 so the code is 0 either way.
+MXQ_HD uint32_t e2m1_mag_short(float a, float s) {
+  float q = a * s;
+  float q1 = fmaf(a, s, 1.0f);
+  int32_t hi = (int32_t)fbits(q) + kHiBias;
+  int32_t lo = (int32_t)fbits(q1) + kLoBias;
+  return (uint32_t)imin(imax(lo, hi), kCodeMax) >> 22;
+}
+
+// Magnitude code of an arbitrary non-negative float32 q (24-bit significand,
+// any size, +inf included).  Below 1 the two midpoints are compared directly;
+// NaN must be handled by the caller.
+MXQ_HD uint32_t e2m1_mag_f32(float q) {
+  int32_t hi = (int32_t)fbits(q) + kHiBias;
+  int32_t lo = ((int32_t)(q > 0.25f) + (int32_t)(q > 0.75f)) << 22;
+  return (uint32_t)imin(imax(lo, hi), kCodeMax) >> 22;
+}
+
+// 2 * e2m1 magnitude for code 0..7: 0 1 2 3 4 6 8 12 (an integer).
+MXQ_HD uint32_t e2m1_twice_mag(uint32_t c) {
+  return (uint32_t)((0x0C08060403020100ull >> (8 * (c & 7))) & 0xFF);
+}
+
+// float32 value of a 4-bit e2m1 code; code 8 (negative zero) gives +0.0.
+MXQ_HD float e2m1_decode(uint32_t c) {
+  int32_t m = (int32_t)e2m1_twice_mag(c);
+  if (c & 8) m = -m;
+  return (float)m * 0.5f;
+}
+
+// ---------------------------------------------------------------- e4m3
+
+// e4m3fn byte of u in [2^-9, 448]: round to nearest, ties to even.
+MXQ_HD uint32_t e4m3_encode_pos(float u) {
+  if (u < 0.015625f) {                       // below 2^-6: quantum 2^-9
+    float r = (u + 16384.0f) - 16384.0f;     // ulp(2^14) = 2^-9: RNE
+    return (uint32_t)(r * 512.0f);           // 1..8 (8 is 2^-6, byte 0x08)
+  }
+  uint32_t b = fbits(u);
+  b = b + 0x7FFFFu + ((b >> 20) & 1u);       // keep 3 mantissa bits, RNE
+  return (b >> 20) - (120u << 3);            // rebias exponent 127 -> 7
+}
+
+// float32 value of a positive e4m3fn byte (0x00..0x7E).
+MXQ_HD float e4m3_decode_pos(uint32_t b) {
+  return b >= 8 ? bitsf((b << 20) + (120u << 23)) : (float)b * 0.001953125f;
+}
+
+// e4m3 round-to-nearest-even of r in [0, 448 * (1 + 2^-23)], returned as a
+// float32 value (saturates at 448): add and remove a power of two whose ulp is
+// the e4m3 quantum of r's binade (2^-9 below 2^-6).
+MXQ_HD float e4m3_round_value(float r) {
+  uint32_t e = fbits(r) >> 23;
+  e = e < 121u ? 121u : e;                   // binades below 2^-6 share 2^-9
+  float c = bitsf((e + 20u) << 23);          // 2^(E + 20): ulp = 2^(E - 3)
+  float v = (r + c) - c;
+  return v > 448.0f ? 448.0f : v;
+}
+
+// ---------------------------------------------------------------- e8m0
+
+// e8m0 byte of the MXFP4 block scale 2^(floor(log2 amax) - 2), clamped below
+// at 2^-127: floor(log2 amax) is the unbiased exponent field, and every amax
+// below 2^-125 (subnormal or zero included) gives byte 0.
+MXQ_HD uint32_t mxfp4_scale_byte(float amax) {
+  uint32_t ex = fbits(amax) >> 23;           // amax >= 0
+  return ex < 2u ? 0u : ex - 2u;
+}
+
+// 2^-(b - 127) as float32 for an e8m0 byte b in [0, 252] (always normal).
+MXQ_HD float e8m0_inverse(uint32_t b) { return bitsf((254u - b) << 23); }
+
+// 2^(b - 128) as float32 (half the e8m0 value, so that twice-magnitude
+// integers times it give e2m1 * 2^(b - 127) exactly); NaN for b = 255.
+MXQ_HD float e8m0_half(uint32_t b) {
+  if (b == 255u) return bitsf(0x7FC00000u);
+  if (b >= 2u) return bitsf((b - 1u) << 23);
+  return bitsf(0x200000u << b);              // 2^-128, 2^-127: subnormal
+}
+
+// ---------------------------------------------------------------- pow2 ceiling
+
+// Smallest power of two >= v for a positive normal float32 v (the cache
+// page's _power_of_two_ceiling): adding 2^23 - 1 to the pattern carries into
+// the exponent exactly when the mantissa is non-zero.
+MXQ_HD float pow2_ceil(float v) { return bitsf((fbits(v) + 0x7FFFFFu) & 0xFF800000u); }
+
+// ---------------------------------------------------------------- rounding to dtype
+
+MXQ_HD uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = fbits(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+MXQ_HD uint32_t f32_to_f16_rne(float f) {
+  _Float16 h = (_Float16)f;   // IEEE round to nearest even (v_cvt_f16_f32)
+  uint16_t u;
+  memcpy(&u, &h, 2);
+  return u;
+}
+
+MXQ_HD float f16_to_f32(uint32_t h) {
+  uint16_t u = (uint16_t)h;
+  _Float16 v;
+  memcpy(&v, &u, 2);
+  return (float)v;
+}
+
+// ---------------------------------------------------------------- exact NVFP4 helpers
+
+// float32 round-to-nearest of a / 6 (a >= 0 finite).  Computed as a binary64
+// product with a correctly rounded 1/6, then one rounding to float32.  This
+// equals the correctly rounded float32 quotient whenever that quotient is a
+// normal number: a / 6 is never a float32 half-way point (its odd part is not
+// dyadic unless 3 divides a's significand, in which case the quotient is
+// exact), its relative distance to the nearest half-way point is at least
+// 2^-27, and the binary64 error is below 2^-52.  Subnormal quotients (a below
+// 6 * 2^-126) use a true division.
+MXQ_HD float div6_rn(float a) {
+  if (a < 8.0e-38f) return a / 6.0f;   // 6 * 2^-126 ~= 7.05e-38
+  return (float)((double)a * (1.0 / 6.0));
+}
+
+// ---------------------------------------------------------------- per-chunk steps
+// The kernels hand 8 consecutive elements (one "chunk", already widened to
+// float32) and the block-level quantities to these functions; the reductions
+// across lanes stay in the kernels.
+
+// MXFP4: packed word of 8 codes (element i in nibble i) given the block's
+// e8m0 byte.  `wide` selects the float32-input rounding (24-bit q).
+MXQ_HD uint32_t mxfp4_quant8(const float f[8], uint32_t sbyte, bool wide) {
+  const float s = e8m0_inverse(sbyte);         // 1 / stored scale, exact
+  uint32_t word = 0;
+  for (int i = 0; i < 8; ++i) {
+    const float m = fabsf(f[i]);
+    const uint32_t mag = wide ? e2m1_mag_f32(m * s) : e2m1_mag_short(m, s);
+    word |= (mag | ((fbits(f[i]) >> 28) & 8u)) << (4 * i);
+  }
+  return word;
+}
+
+// MXFP4 decode of a packed word into 8 float32 values e2m1 * 2^(b - 127).
+MXQ_HD void mxfp4_dequant8(uint32_t w, uint32_t sbyte, float out[8]) {
+  const float s = e8m0_half(sbyte);            // 2^(b - 128)
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t code = (w >> (4 * i)) & 15u;
+    int32_t m = (int32_t)e2m1_twice_mag(code);
+    m = (code & 8u) ? -m : m;                  // -0 -> +0
+    out[i] = (float)m * s;                     // exact
+  }
+}
+
+// NVFP4 block scale from the block amax a and the row scale g:
+// e4m3(clamp((a / 6) / g, 2^-9, 448)), a NaN ratio taking 2^-9; returns the
+// byte and the divisor block_scale * g.
+MXQ_HD uint32_t nvfp4_block_scale(float a, float g, float* den) {
+  float u = a / 6.0f;
+  u = u / g;
+  u = fminf(fmaxf(u, 0.001953125f), 448.0f);
+  const uint32_t sb = e4m3_encode_pos(u);
+  *den = e4m3_decode_pos(sb) * g;
+  return sb;
+}
+
+// NVFP4: packed word of 8 codes for elements divided by `den`.
+MXQ_HD uint32_t nvfp4_quant8(const float f[8], float den) {
+  uint32_t word = 0;
+  for (int i = 0; i < 8; ++i) {
+    float q = fabsf(f[i]) / den;               // correctly rounded
+    q = (q == q) ? q : 0.0f;                   // 0 / 0 -> code 0
+    word |= (e2m1_mag_f32(q) | ((fbits(f[i]) >> 28) & 8u)) << (4 * i);
+  }
+  return word;
+}
+
+// Any e4m3fn byte: sign, NaN for 0x7F / 0xFF.
+MXQ_HD float e4m3_decode_any(uint32_t b) {
+  const uint32_t m = b & 0x7Fu;
+  const float v = (m == 0x7Fu) ? bitsf(0x7FC00000u) : e4m3_decode_pos(m);
+  return (b & 0x80u) ? -v : v;
+}
+
+// NVFP4 decode: (e2m1 * e4m3) * g in float32, left to right.
+MXQ_HD void nvfp4_dequant8(uint32_t w, uint32_t sbyte, float g, float out[8]) {
+  const float sigma = e4m3_decode_any(sbyte);
+  for (int i = 0; i < 8; ++i) {
+    const float t = e2m1_decode((w >> (4 * i)) & 15u) * sigma;   // exact
+    out[i] = t * g;
+  }
+}
+
+// Cache round trip: the per-group scale and the per-element image.
+struct CacheGroupScale {
+  float inv;     // multiplier into the quantized domain (fp8, mxfp4)
+  float s;       // the group scale (power of two, or the e4m3 value)
+  float half_s;  // s / 2: twice-magnitude integers times this are e2m1 * s
+};
+
+MXQ_HD CacheGroupScale cache_scale(int fmt, float a) {
+  CacheGroupScale r;
+  if (fmt == FMT_FP8 || fmt == FMT_MXFP4) {
+    const float v = fmaxf(a / (fmt == FMT_FP8 ? 448.0f : 6.0f), 1.17549435e-38f);
+    r.s = pow2_ceil(v);
+    r.inv = bitsf((254u - (fbits(r.s) >> 23)) << 23);   // 2^-k, exact
+  } else {
+    const float u = fminf(fmaxf(a / 6.0f, 0.001953125f), 448.0f);
+    r.s = e4m3_decode_pos(e4m3_encode_pos(u));
+    r.inv = 0.0f;                                      // nvfp4 divides by s
+  }
+  r.half_s = r.s * 0.5f;
+  return r;
+}
+
+// `wide`: float32 input (24-bit significands) for the mxfp4 rounding.
+MXQ_HD float cache_qdq1(int fmt, bool wide, float x, const CacheGroupScale& g) {
+  const float m = fabsf(x);
+  if (fmt == FMT_FP8) {
+    const float v = e4m3_round_value(m * g.inv) * g.s;  // exact product
+    return copysignf(v, x);                             // sign of zero kept
+  }
+  uint32_t mag;
+  if (fmt == FMT_MXFP4)
+    mag = wide ? e2m1_mag_f32(m * g.inv) : e2m1_mag_short(m, g.inv);
+  else
+    mag = e2m1_mag_f32(m / g.s);                        // correctly rounded
+  int32_t t = (int32_t)e2m1_twice_mag(mag);
+  t = (fbits(x) >> 31) ? -t : t;                        // -0 -> +0
+  return (float)t * g.half_s;                           // exact
+}
+
+} // namespace mxq

@@ -1,0 +1,184 @@
+/*
+ * mxq.h -- C ABI of libmxq: block-scaled microscaling quantization on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Three operations along the last dimension of a contiguous row-major
+ * [rows, K] tensor:
+ *   - quantize-pack into e2m1 (fp4) nibbles plus per-block scales
+ *     (MXFP4: one e8m0 scale per 32 columns; NVFP4: one e4m3 scale per 16
+ *     columns plus one float32 scale per row),
+ *   - dequantize back to a floating dtype,
+ *   - the quantize/dequantize round trip used for cache values (fp8 e4m3,
+ *     mxfp4 or nvfp4 groups of any block size).
+ *
+ * Sources, cited by page title and section:
+ *   [mxfp4 page] "nemo_automodel.components.quantization.mxfp4"
+ *   [nvfp4 page] "nemo_automodel.components.quantization.nvfp4"
+ *   [cache page] "nemo_automodel.components.models.deepseek_v41.quantization"
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is a DEVICE pointer to contiguous row-major memory
+ *     owned by the caller; the library allocates nothing and keeps no state.
+ *     "rows" is the product of all leading dimensions.
+ *   - Alignment: float/bfloat16/float16 tensors and packed arrays must be
+ *     16-byte aligned for the weight calls (MXQ_E_ALIGN otherwise); the cache
+ *     call accepts any alignment (it takes a slower path when x or y is not
+ *     16-byte aligned or C is not a multiple of 8).
+ *   - Calls are asynchronous on `stream` (0 = the null stream): argument
+ *     validation happens synchronously on the host and returns an error
+ *     status before anything is launched; a successful call returns MXQ_OK
+ *     once its kernels are enqueued and never synchronizes.  A launch failure
+ *     reported by the runtime returns MXQ_E_LAUNCH.
+ *   - rows == 0 or K == 0 is valid and launches nothing.
+ *   - Inputs are never written.  Outputs must not overlap inputs.
+ *   - Thread-safe: no global state.
+ *   - Packed nibble order: the even column in the low nibble, the following
+ *     odd column in the high nibble ([mxfp4 page] and [nvfp4 page],
+ *     introductions).
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+
+/* Floating element types of inputs and dequantized outputs ([mxfp4 page]
+ * and [nvfp4 page] take any floating-point tensor). */
+typedef enum mxq_dtype {
+  MXQ_F32 = 0,
+  MXQ_BF16 = 1,
+  MXQ_F16 = 2
+} mxq_dtype;
+
+/* Cache value formats ([cache page], quantize_cache: fp8 for SWA KV, mxfp4
+ * with an E8M0 scale for index Q/K, nvfp4 with an E4M3 scale for compressed
+ * KV). */
+typedef enum mxq_format {
+  MXQ_FMT_FP8 = 0,
+  MXQ_FMT_MXFP4 = 1,
+  MXQ_FMT_NVFP4 = 2
+} mxq_format;
+
+/* How mxq_quantize_nvfp4 obtains the float32 scale g of each row. */
+typedef enum mxq_nv_mode {
+  /* g = amax(row) / (6 * 448) for every row ([nvfp4 page] quantize_nvfp4,
+   * default rule: one global scale per row). */
+  MXQ_NV_ROW_AMAX = 0,
+  /* g = given[r * given_stride]: caller-supplied scales ([nvfp4 page]
+   * quantize_nvfp4 with global_scale); given_stride 1 = one per row, 0 = one
+   * for the whole tensor. */
+  MXQ_NV_GIVEN = 1,
+  /* g = amax(whole tensor) / (6 * 448), written to every row_scale entry
+   * ([nvfp4 page] quantize_nvfp4_modelopt: one tensor scale). Needs
+   * `scratch`: 4 bytes of device memory that receive the tensor amax. */
+  MXQ_NV_TENSOR_AMAX = 2
+} mxq_nv_mode;
+
+typedef enum mxq_status {
+  MXQ_OK = 0,
+  MXQ_E_NULL = 1,    /* a required pointer is NULL                           */
+  MXQ_E_SHAPE = 2,   /* negative size, or K not a whole number of blocks     */
+  MXQ_E_DTYPE = 3,   /* unknown mxq_dtype                                    */
+  MXQ_E_FORMAT = 4,  /* unknown mxq_format                                   */
+  MXQ_E_BLOCK = 5,   /* cache block_size < 1                                 */
+  MXQ_E_SIZE = 6,    /* rows * K overflows int64                             */
+  MXQ_E_LAUNCH = 7,  /* the HIP runtime rejected a kernel launch             */
+  MXQ_E_MODE = 8,    /* unknown mxq_nv_mode                                  */
+  MXQ_E_ALIGN = 9    /* a pointer is not 16-byte aligned where required      */
+} mxq_status;
+
+/*
+ * MXFP4 quantize ([mxfp4 page] quantize_mxfp4).
+ *   x       [rows, K] of xdt; K % 32 == 0, else MXQ_E_SHAPE.
+ *   packed  [rows, K/2] int8: two e2m1 codes per byte.
+ *   scales  [rows, K/32] float8_e8m0fnu bytes: for each 32-column block the
+ *           scale 2^(floor(log2(amax)) - 2), floor exact, clamped below at
+ *           2^-127 (byte 0; also for an all-zero block).  Elements are divided
+ *           by the stored scale and rounded to the nearest e2m1 value (ties to
+ *           the smaller magnitude); the sign nibble bit is the input's sign.
+ */
+mxq_status mxq_quantize_mxfp4(const void* x, mxq_dtype xdt, int64_t rows,
+                              int64_t K, int8_t* packed, uint8_t* scales,
+                              hipStream_t stream);
+
+/*
+ * MXFP4 dequantize ([mxfp4 page] dequantize_mxfp4).
+ *   packed [rows, K/2] int8, scales [rows, K/32] e8m0 bytes (K % 32 == 0).
+ *   y      [rows, K] of ydt: e2m1(code) * 2^(scale - 127), computed exactly in
+ *          float32 and rounded once to ydt (code 8 decodes to +0.0; scale byte
+ *          0xFF gives NaN).
+ */
+mxq_status mxq_dequantize_mxfp4(const int8_t* packed, const uint8_t* scales,
+                                int64_t rows, int64_t K, void* y,
+                                mxq_dtype ydt, hipStream_t stream);
+
+/*
+ * NVFP4 quantize ([nvfp4 page] quantize_nvfp4, quantize_nvfp4_modelopt;
+ * K % 16 == 0 else MXQ_E_SHAPE, the rule of _check_last_dim).
+ *   Per row: g as selected by `mode` (float32).  Per 16-column block with
+ *   amax a: block scale = e4m3(clamp((a / 6) / g, 2^-9, 448)); each element is
+ *   divided by (block scale * g) and rounded to the nearest e2m1 value (ties to
+ *   the smaller magnitude).  All arithmetic is float32, correctly rounded,
+ *   evaluated in that order.
+ *   given, given_stride   used by MXQ_NV_GIVEN only (device pointer).
+ *   scratch               MXQ_NV_TENSOR_AMAX only: 4 bytes of device memory,
+ *                         overwritten with the tensor amax.
+ *   packed     [rows, K/2] uint8 (same bits as int8).
+ *   scales     [rows, K/16] float8_e4m3fn bytes.
+ *   row_scale  [rows] float32: the g used for each row.
+ *   The ModelOpt NVFP4 layout: 0.5625 bytes per parameter plus 4 bytes per
+ *   row ([nvfp4 page] introduction).
+ */
+mxq_status mxq_quantize_nvfp4(const void* x, mxq_dtype xdt, int64_t rows,
+                              int64_t K, mxq_nv_mode mode, const float* given,
+                              int64_t given_stride, float* scratch,
+                              uint8_t* packed, uint8_t* scales,
+                              float* row_scale, hipStream_t stream);
+
+/*
+ * NVFP4 dequantize ([nvfp4 page] dequantize_nvfp4).
+ *   packed [rows, K/2] uint8 or int8 bits, scales [rows, K/16] e4m3 bytes,
+ *   row_scale [rows] float32.
+ *   y [rows, K] of ydt: (e2m1(code) * e4m3(scale)) * row_scale in float32,
+ *   left to right, then one rounding to ydt.
+ */
+mxq_status mxq_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales,
+                                const float* row_scale, int64_t rows,
+                                int64_t K, void* y, mxq_dtype ydt,
+                                hipStream_t stream);
+
+/*
+ * Cache quantize/dequantize round trip ([cache page] quantize_cache and
+ * _CacheQuantization.forward): y gets x's shape [rows, C] and dtype.
+ *   Groups are block_size consecutive channels (block_size >= 1, else
+ *   MXQ_E_BLOCK); a last partial group behaves as if zero-padded.  Per group
+ *   with amax a:
+ *     MXQ_FMT_FP8:   s = pow2ceil(max(a / 448, 2^-126)); y = e4m3(x / s) * s
+ *                    (e4m3 round to nearest even; the sign of zero is kept);
+ *     MXQ_FMT_MXFP4: s = pow2ceil(max(a / 6, 2^-126)); y = e2m1(x / s) * s;
+ *     MXQ_FMT_NVFP4: s = e4m3(clamp(a / 6, 2^-9, 448));  y = e2m1(x / s) * s;
+ *   pow2ceil is the [cache page] _power_of_two_ceiling; e2m1 rounds to the
+ *   nearest value with ties to the smaller magnitude and decodes code 8 to
+ *   +0.0.  The products are exact in float32; y is rounded once to dt.
+ *   x and y must not overlap.
+ */
+mxq_status mxq_quantize_cache(const void* x, void* y, mxq_dtype dt,
+                              int64_t rows, int64_t C, mxq_format fmt,
+                              int32_t block_size, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* mxq_status_string(mxq_status s);
+
+/* MXQ_ABI_VERSION of the loaded library. */
+int32_t mxq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXQ_H */

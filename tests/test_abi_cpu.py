@@ -1,0 +1,108 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/mxq.h declares, and rejects bad arguments with the documented
+status before touching the device (no compute calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "mxq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_operations():
+    names = _declared_functions()
+    for n in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
+              "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_status_string",
+              "mxq_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import fp8_quantize_pack_amd as mxq
+    for n in _declared_functions():
+        assert hasattr(mxq.lib, n), n
+    assert mxq.abi_version() == 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    import fp8_quantize_pack_amd as mxq
+    return mxq.lib
+
+
+FAKE = 1 << 20     # an aligned non-null address; never dereferenced here
+
+
+def test_quantize_mxfp4_validation(L):
+    f = L.mxq_quantize_mxfp4
+    assert f(FAKE, 1, 4, 48, FAKE, FAKE, None) == 2           # K % 32
+    assert f(FAKE, 1, -1, 64, FAKE, FAKE, None) == 2          # rows < 0
+    assert f(FAKE, 7, 4, 64, FAKE, FAKE, None) == 3           # dtype
+    assert f(FAKE, 1, 1 << 40, 1 << 30, FAKE, FAKE, None) == 6  # overflow
+    assert f(None, 1, 4, 64, FAKE, FAKE, None) == 1
+    assert f(FAKE, 1, 4, 64, None, FAKE, None) == 1
+    assert f(FAKE + 2, 1, 4, 64, FAKE, FAKE, None) == 9       # alignment
+    assert f(None, 1, 0, 64, None, None, None) == 0           # empty: no launch
+    assert f(None, 1, 5, 0, None, None, None) == 0
+
+
+def test_dequantize_mxfp4_validation(L):
+    f = L.mxq_dequantize_mxfp4
+    assert f(FAKE, FAKE, 4, 40, FAKE, 1, None) == 2
+    assert f(FAKE, FAKE, 4, 64, FAKE, 9, None) == 3
+    assert f(FAKE, None, 4, 64, FAKE, 1, None) == 1
+    assert f(FAKE, FAKE, 4, 64, FAKE + 8, 1, None) == 9
+    assert f(None, None, 0, 64, None, 1, None) == 0
+
+
+def test_quantize_nvfp4_validation(L):
+    f = L.mxq_quantize_nvfp4
+    args = lambda **k: dict(dict(x=FAKE, dt=1, rows=4, K=64, mode=0, given=None, gs=1,
+                                 scratch=None, p=FAKE, s=FAKE, rs=FAKE, st=None), **k)
+    call = lambda a: f(a["x"], a["dt"], a["rows"], a["K"], a["mode"], a["given"], a["gs"],
+                       a["scratch"], a["p"], a["s"], a["rs"], a["st"])
+    assert call(args(K=40)) == 2                      # not a whole number of 16-col blocks
+    assert call(args(dt=5)) == 3
+    assert call(args(mode=3)) == 8
+    assert call(args(mode=1, given=None)) == 1
+    assert call(args(mode=1, given=FAKE, gs=2)) == 2
+    assert call(args(mode=2, scratch=None)) == 1
+    assert call(args(rs=None)) == 1
+    assert call(args(x=FAKE + 4)) == 9
+    assert call(args(rows=0, x=None, p=None, s=None, rs=None)) == 0
+
+
+def test_quantize_cache_validation(L):
+    f = L.mxq_quantize_cache
+    assert f(FAKE, FAKE, 1, 4, 64, 3, 32, None) == 4   # format
+    assert f(FAKE, FAKE, 1, 4, 64, 0, 0, None) == 5    # block size
+    assert f(FAKE, FAKE, 4, 4, 64, 0, 32, None) == 3   # dtype
+    assert f(None, FAKE, 1, 4, 64, 0, 32, None) == 1
+    assert f(None, None, 1, 0, 64, 0, 32, None) == 0
+    assert f(FAKE, FAKE, 1, -2, 64, 0, 32, None) == 2
+
+
+def test_status_strings(L):
+    for s in range(10):
+        assert L.mxq_status_string(s)
+    assert L.mxq_status_string(99) == b"unknown status"
+
+
+def test_python_wrapper_raises_page_errors_on_cpu_tensors():
+    import torch
+    import fp8_quantize_pack_amd as mxq
+    with pytest.raises(ValueError, match="divisible by 32"):
+        mxq.quantize_mxfp4(torch.zeros(2, 48))
+    with pytest.raises(ValueError, match="16-column blocks"):
+        mxq.quantize_nvfp4(torch.zeros(2, 40))
+    with pytest.raises(ValueError, match="GPU"):
+        mxq.quantize_mxfp4(torch.zeros(2, 64))
+    with pytest.raises(ValueError, match="cache format"):
+        mxq.quantize_cache(torch.zeros(2, 64), "int4", 32)

@@ -1,0 +1,423 @@
+"""GPU parity: libmxq (through its C ABI) against the CPU oracle, bit for bit.
+
+Small and ragged shapes are compared whole; the full-size workloads are
+compared on sampled rows (every operation is row-local, so a sampled row's
+oracle result is computed from that row alone), in the same launch
+configuration the bench uses.  Every output buffer sits between guard bands
+filled with 0xA5 that must survive the call.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+DEV = "cuda"
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_quantize_pack_amd  # noqa: F401  (fails loudly when not built)
+    yield
+
+
+def mxq():
+    import fp8_quantize_pack_amd as m
+    return m
+
+
+def guarded(shape, dtype):
+    """Output tensor with 4 KiB guard bands of 0xA5 on both sides."""
+    n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+    raw = torch.full((GUARD + n + GUARD,), 0xA5, dtype=torch.uint8, device=DEV)
+    t = raw[GUARD:GUARD + n].view(dtype).view(*shape)
+    return raw, t
+
+
+def check_guard(raw):
+    torch.cuda.synchronize()
+    assert bool((raw[:GUARD] == 0xA5).all()) and bool((raw[-GUARD:] == 0xA5).all()), "guard band overwritten"
+
+
+def bits(t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.float32,):
+        return t.view(torch.int32)
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16)
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e8m0fnu, torch.int8):
+        return t.view(torch.uint8)
+    return t
+
+
+def assert_same(gpu, ref, what):
+    g, r = bits(gpu), bits(ref)
+    if not torch.equal(g, r):
+        bad = (g != r).nonzero()
+        raise AssertionError(f"{what}: {bad.shape[0]} mismatches, first at {bad[:5].tolist()}: "
+                             f"gpu={g[tuple(bad[0])].item()} oracle={r[tuple(bad[0])].item()}")
+
+
+# ------------------------------------------------------------------ runners (C ABI)
+
+def gpu_quantize_mxfp4(x):
+    K = x.shape[-1]
+    rp, p = guarded((*x.shape[:-1], K // 2), torch.int8)
+    rs, s = guarded((*x.shape[:-1], K // 32), torch.uint8)
+    mxq().mxq_quantize_mxfp4(x, p, s)
+    check_guard(rp); check_guard(rs)
+    return p, s
+
+
+def gpu_dequantize_mxfp4(p, s, dtype):
+    K = p.shape[-1] * 2
+    ry, y = guarded((*p.shape[:-1], K), dtype)
+    mxq().mxq_dequantize_mxfp4(p, s, y)
+    check_guard(ry)
+    return y
+
+
+def gpu_quantize_nvfp4(x, mode="row", given=None):
+    K = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    rp, p = guarded((*lead, K // 2), torch.uint8)
+    rs, s = guarded((*lead, K // 16), torch.uint8)
+    rg, g = guarded(lead if lead else (1,), torch.float32)
+    scratch = torch.zeros(1, dtype=torch.float32, device=DEV)
+    stride = 1
+    if mode == "given":
+        stride = 0 if given.numel() == 1 else 1
+        given = given.to(DEV, torch.float32).contiguous()
+    mxq().mxq_quantize_nvfp4(x, p, s, g, mode=mode, given=given, given_stride=stride,
+                             scratch=scratch)
+    check_guard(rp); check_guard(rs); check_guard(rg)
+    return p, s, g
+
+
+def gpu_dequantize_nvfp4(p, s, g, dtype):
+    K = p.shape[-1] * 2
+    ry, y = guarded((*p.shape[:-1], K), dtype)
+    mxq().mxq_dequantize_nvfp4(p, s, g, y)
+    check_guard(ry)
+    return y
+
+
+def gpu_quantize_cache(x, fmt, B):
+    ry, y = guarded(tuple(x.shape), x.dtype)
+    mxq().mxq_quantize_cache(x, y, fmt, B)
+    check_guard(ry)
+    return y
+
+
+# ------------------------------------------------------------------ MXFP4
+
+MX_SHAPES = [(3, 5, 96), (257, 1024), (1, 32), (4100, 64)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("shape", MX_SHAPES)
+def test_mxfp4_roundtrip_small(shape, dtype):
+    say("mxfp4 small", shape, dtype)
+    x = synth.moe_mxfp4(shape, seed=sum(shape)).to(dtype)
+    po, so = oracle.quantize_mxfp4(x)
+    p, s = gpu_quantize_mxfp4(x.to(DEV))
+    assert_same(s, so, "scales")
+    assert_same(p, po, "packed")
+    for odt in (torch.float32, torch.bfloat16, torch.float16):
+        yo = oracle.dequantize_mxfp4(po, so, odt)
+        y = gpu_dequantize_mxfp4(p, s, odt)
+        assert_same(y, yo, f"dequant {odt}")
+
+
+def test_mxfp4_config1_fp32_with_zero_and_tiny_rows():
+    say("mxfp4 fp32 [256,1024] with zero row and 1e-30 row")
+    x = synth.mxfp4_fp32()
+    po, so = oracle.quantize_mxfp4(x)
+    p, s = gpu_quantize_mxfp4(x.to(DEV))
+    assert_same(s, so, "scales")
+    assert_same(p, po, "packed")
+    assert_same(gpu_dequantize_mxfp4(p, s, torch.float32), oracle.dequantize_mxfp4(po, so, torch.float32), "dequant")
+
+
+def test_mxfp4_exhaustive_bf16_under_every_scale():
+    """All bf16 values that fit a block, under each of the 253 e8m0 scales
+    (the GPU's IEEE behaviour on subnormals and on midpoints included)."""
+    say("mxfp4 exhaustive bf16 x scales")
+    bitsv = np.arange(1 << 16, dtype=np.uint32)
+    allv = (bitsv << 16).view(np.float32)
+    allv = allv[np.isfinite(allv)]
+    expo = (allv.view(np.uint32) >> 23) & 0xFF
+    rows = []
+    for sb in range(253):
+        vals = allv[expo <= sb + 2]
+        anchor = np.float32(2.0 ** (sb - 125)) if sb > 0 else np.float32(2.0 ** -125)
+        vals = np.concatenate([vals, np.zeros((-vals.size) % 31, np.float32)]).reshape(-1, 31)
+        rows.append(np.concatenate([np.full((vals.shape[0], 1), anchor, np.float32), vals], 1))
+    x = torch.from_numpy(np.concatenate(rows)).to(torch.bfloat16)
+    po, so = oracle.quantize_mxfp4(x)
+    p, s = gpu_quantize_mxfp4(x.to(DEV))
+    assert_same(s, so, "scales")
+    assert_same(p, po, "packed")
+    assert_same(gpu_dequantize_mxfp4(p, s, torch.bfloat16),
+                oracle.dequantize_mxfp4(po, so, torch.bfloat16), "dequant")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_mxfp4_dequant_every_byte_every_scale(dtype):
+    say("mxfp4 dequant all bytes x scales", dtype)
+    p = torch.arange(256, dtype=torch.uint8).repeat(256, 1).view(torch.int8)
+    s = torch.arange(256, dtype=torch.uint8).reshape(256, 1).repeat(1, 16)
+    yo = oracle.dequantize_mxfp4(p.view(torch.uint8), s, dtype)
+    y = gpu_dequantize_mxfp4(p.to(DEV), s.to(DEV), dtype).cpu()
+    nan = torch.isnan(yo.float())
+    assert torch.equal(nan, torch.isnan(y.float()))
+    assert_same(y[~nan], yo[~nan], "dequant")
+
+
+def test_mxfp4_empty_inputs_launch_nothing():
+    say("mxfp4 empty")
+    for shape in ((0, 64), (3, 0)):
+        x = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        p, s = mxq().quantize_mxfp4(x)
+        assert p.shape == (*shape[:-1], shape[-1] // 2)
+        y = mxq().dequantize_mxfp4(p, s, torch.bfloat16)
+        assert y.shape == shape
+
+
+# ------------------------------------------------------------------ NVFP4
+
+NV_SHAPES = [(5, 16), (7, 48), (33, 512), (9, 2064), (6, 4096), (5, 7168), (3, 8208), (2, 3, 256)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("shape", NV_SHAPES)
+def test_nvfp4_row_mode_small(shape, dtype):
+    say("nvfp4 row", shape, dtype)
+    x = synth.moe_nvfp4(shape, seed=sum(shape)).to(dtype)
+    po, so, go = oracle.quantize_nvfp4(x)
+    p, s, g = gpu_quantize_nvfp4(x.to(DEV))
+    assert_same(g, go, "row scale")
+    assert_same(s, so, "scales")
+    assert_same(p, po, "packed")
+    for odt in (torch.bfloat16, torch.float32, torch.float16):
+        assert_same(gpu_dequantize_nvfp4(p, s, g, odt), oracle.dequantize_nvfp4(po, so, go, odt),
+                    f"dequant {odt}")
+
+
+def test_nvfp4_sweep_specials():
+    say("nvfp4 sweep specials")
+    x = synth.moe_sweep((2, 64, 7168), seed=11, special_frac=0.02)
+    po, so, go = oracle.quantize_nvfp4(x)
+    p, s, g = gpu_quantize_nvfp4(x.to(DEV))
+    assert_same(g, go, "row scale"); assert_same(s, so, "scales"); assert_same(p, po, "packed")
+    assert_same(gpu_dequantize_nvfp4(p, s, g, torch.bfloat16),
+                oracle.dequantize_nvfp4(po, so, go, torch.bfloat16), "dequant")
+
+
+@pytest.mark.parametrize("kind", ["pow2", "random", "scalar", "edge"])
+def test_nvfp4_given_scales(kind):
+    say("nvfp4 given", kind)
+    rng = np.random.default_rng(3)
+    R, K = 96, 256
+    x = torch.from_numpy(rng.standard_normal((R, K)).astype(np.float32)).to(torch.bfloat16)
+    if kind == "pow2":
+        gv = torch.from_numpy(np.exp2(rng.integers(-12, -2, R)).astype(np.float32))
+    elif kind == "random":
+        gv = torch.from_numpy((rng.random(R) * 1e-3).astype(np.float32))
+    elif kind == "scalar":
+        gv = torch.tensor([3.7e-4])
+    else:
+        x[3] = 0
+        gv = torch.from_numpy(np.resize(np.array([0.0, 1e-42, 1e30, np.inf, 2.0 ** -126, 3.0, 1e-20, 1e20],
+                                                 np.float32), R))
+    po, so, go = oracle.quantize_nvfp4(x, mode="given", given=gv)
+    p, s, g = gpu_quantize_nvfp4(x.to(DEV), mode="given", given=gv)
+    assert_same(g, go, "row scale"); assert_same(s, so, "scales"); assert_same(p, po, "packed")
+
+
+@pytest.mark.parametrize("shape", [(64, 128), (300, 4096), (17, 16)])
+def test_nvfp4_tensor_mode(shape):
+    say("nvfp4 tensor mode", shape)
+    x = synth.moe_nvfp4(shape, seed=shape[0])
+    po, so, go = oracle.quantize_nvfp4(x, mode="tensor")
+    p, s, g = gpu_quantize_nvfp4(x.to(DEV), mode="tensor")
+    assert_same(g, go, "row scale"); assert_same(s, so, "scales"); assert_same(p, po, "packed")
+    pw, sw, gw = mxq().quantize_nvfp4_modelopt(x.to(DEV))
+    assert_same(pw, po, "modelopt packed"); assert_same(sw, so, "modelopt scales")
+    assert gw.item() == go[0].item()
+
+
+def test_nvfp4_zero_rows():
+    say("nvfp4 zero rows")
+    x = torch.zeros(8, 64, dtype=torch.bfloat16)
+    x[3, 5] = 1.0
+    po, so, go = oracle.quantize_nvfp4(x)
+    p, s, g = gpu_quantize_nvfp4(x.to(DEV))
+    assert_same(g, go, "row scale"); assert_same(s, so, "scales"); assert_same(p, po, "packed")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_nvfp4_dequant_every_code_every_scale(dtype):
+    say("nvfp4 dequant all codes x scales", dtype)
+    rng = np.random.default_rng(8)
+    R = 64
+    p = torch.arange(256, dtype=torch.uint8).repeat(R, 8)
+    s = torch.arange(256, dtype=torch.uint8).repeat(R, 1)
+    g = torch.from_numpy(np.concatenate([np.exp2(rng.random(R - 6) * 60 - 40),
+                                         [0.0, 1e-40, 3e38, 2.0 ** -126, 1.0, 6e4]]).astype(np.float32))
+    yo = oracle.dequantize_nvfp4(p, s, g, dtype)
+    y = gpu_dequantize_nvfp4(p.to(DEV), s.to(DEV), g.to(DEV), dtype).cpu()
+    nan = torch.isnan(yo.float())
+    assert torch.equal(nan, torch.isnan(y.float()))
+    assert_same(y[~nan], yo[~nan], "dequant")
+
+
+# ------------------------------------------------------------------ cache
+
+CACHE_CASES = [(512, 32), (128, 32), (512, 16), (120, 32), (100, 16), (96, 7), (64, 64),
+               (1024, 512), (40, 8), (24, 256)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "nvfp4"])
+@pytest.mark.parametrize("C,B", CACHE_CASES)
+def test_cache_small(C, B, fmt, dtype):
+    say("cache", fmt, C, B, dtype)
+    x = synth.kv_cache((3, 37, C), seed=C * 7 + B).to(dtype)
+    x[0, 0] = 0
+    x[0, 1] = x[0, 1] * 2.0 ** -125
+    x[0, 2, :8] = -0.0
+    yo = oracle.quantize_cache(x, fmt, B)
+    y = gpu_quantize_cache(x.to(DEV), fmt, B)
+    assert_same(y, yo, "qdq")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "nvfp4"])
+def test_cache_unaligned_views(fmt):
+    say("cache unaligned", fmt)
+    x = synth.kv_cache((5, 129), seed=1)
+    xo = x[:, 1:]                           # C = 128, rows start 2 bytes off
+    yo = oracle.quantize_cache(xo.contiguous(), fmt, 32)
+    xd = x.to(DEV)[:, 1:]
+    raw = torch.full((5 * 129 + 64,), 0, dtype=torch.bfloat16, device=DEV)
+    ydst = raw[1:1 + 5 * 128].view(5, 128)  # misaligned output
+    mxq().mxq_quantize_cache(xd.contiguous()[:, :], ydst, fmt, 32)
+    assert_same(ydst, yo, "qdq")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "nvfp4"])
+def test_cache_all_bf16_values(fmt):
+    say("cache all bf16 values", fmt)
+    bitsv = np.arange(1 << 16, dtype=np.uint32)
+    v = (bitsv << 16).view(np.float32)
+    v = torch.from_numpy(v[np.isfinite(v)]).to(torch.bfloat16)
+    v = v[torch.randperm(v.numel(), generator=torch.Generator().manual_seed(3))]
+    v = torch.nn.functional.pad(v, (0, (-v.numel()) % 32)).reshape(-1, 32)
+    for B in (32, 16):
+        assert_same(gpu_quantize_cache(v.to(DEV), fmt, B), oracle.quantize_cache(v, fmt, B), f"B={B}")
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled rows)
+
+def _sample_rows(R, n, seed, must=()):
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.randperm(R, generator=g)[:n]
+    idx = torch.cat([idx, torch.tensor([0, R - 1] + list(must), dtype=torch.long)])
+    return torch.unique(idx)
+
+
+def test_full_c2_mxfp4_moe():
+    say("full C2 mxfp4 [32,4096,2048]")
+    x = synth.moe_mxfp4(synth.SHAPES["c2"], device=DEV).reshape(-1, 2048)
+    p, s = mxq().quantize_mxfp4(x)
+    y = mxq().dequantize_mxfp4(p, s, torch.bfloat16)
+    idx = _sample_rows(x.shape[0], 1500, 2)
+    xs = x[idx.to(DEV)].cpu()
+    po, so = oracle.quantize_mxfp4(xs)
+    assert_same(s[idx.to(DEV)], so, "scales")
+    assert_same(p[idx.to(DEV)], po, "packed")
+    assert_same(y[idx.to(DEV)], oracle.dequantize_mxfp4(po, so, torch.bfloat16), "dequant")
+    # idempotence over the whole tensor
+    p2, s2 = mxq().quantize_mxfp4(y)
+    assert torch.equal(mxq().dequantize_mxfp4(p2, s2, torch.bfloat16).view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("given_half", [False, True])
+def test_full_c3_nvfp4_gate_up(given_half):
+    say("full C3 nvfp4 [64,3072,4096] given_half=", given_half)
+    x = synth.moe_nvfp4(synth.SHAPES["c3"], device=DEV)
+    E, N, K = x.shape
+    if given_half:
+        amax_half = x.float().abs().reshape(E, 2, N // 2, K).amax(dim=(2, 3))
+        gvals = (amax_half / 2688.0).reshape(E, 2, 1).expand(E, 2, N // 2).reshape(E, N)
+        p, s, g = mxq().quantize_nvfp4(x, global_scale=gvals)
+    else:
+        p, s, g = mxq().quantize_nvfp4(x)
+    y = mxq().dequantize_nvfp4(p, s, g, torch.bfloat16)
+    xf = x.reshape(-1, K)
+    idx = _sample_rows(xf.shape[0], 1200, 3).to(DEV)
+    xs = xf[idx].cpu()
+    if given_half:
+        po, so, go = oracle.quantize_nvfp4(xs, mode="given", given=gvals.reshape(-1)[idx].cpu())
+    else:
+        po, so, go = oracle.quantize_nvfp4(xs)
+    assert_same(g.reshape(-1)[idx], go, "row scale")
+    assert_same(s.reshape(-1, K // 16)[idx], so, "scales")
+    assert_same(p.reshape(-1, K // 2)[idx], po, "packed")
+    assert_same(y.reshape(-1, K)[idx], oracle.dequantize_nvfp4(po, so, go, torch.bfloat16), "dequant")
+
+
+@pytest.mark.parametrize("case,fmt,B", [("c4a", "fp8", 32), ("c4b", "mxfp4", 32), ("c4c", "nvfp4", 16)])
+def test_full_c4_cache(case, fmt, B):
+    say("full", case, fmt)
+    x = synth.kv_cache(synth.SHAPES[case], seed=synth.SEEDS[case], device=DEV)
+    y = mxq().quantize_cache(x, fmt, B)
+    assert y.shape == x.shape and y.dtype == x.dtype
+    C = x.shape[-1]
+    xf, yf = x.reshape(-1, C), y.reshape(-1, C)
+    idx = _sample_rows(xf.shape[0], 3000, 4).to(DEV)
+    assert_same(yf[idx], oracle.quantize_cache(xf[idx].cpu(), fmt, B), "qdq")
+
+
+def test_full_c5_chunk_mxfp4_nvfp4():
+    """One 36-expert chunk of the large sweep (about 1 GiB of bf16), as the
+    bench processes it; rows holding zero, subnormal and spike blocks are
+    always among the sampled rows."""
+    cid, e0, ne = synth.c5_chunks()[0]
+    say("full C5 chunk", cid, ne, "experts")
+    x = synth.c5_chunk(cid, ne, device=DEV)
+    K = x.shape[-1]
+    xf = x.reshape(-1, K)
+    blocks = xf.view(xf.shape[0], K // 32, 32)
+    bmax = blocks.float().abs().amax(-1)
+    special_rows = torch.nonzero(((bmax == 0) | (bmax < 1e-30) | (bmax > 1e3)).any(-1)).reshape(-1)
+    must = special_rows[torch.randperm(special_rows.numel(), device=DEV)[:300]].cpu().tolist()
+    idx = _sample_rows(xf.shape[0], 1200, 5, must).to(DEV)
+    xs = xf[idx].cpu()
+    p, s = mxq().quantize_mxfp4(x)
+    y = mxq().dequantize_mxfp4(p, s, torch.bfloat16)
+    po, so = oracle.quantize_mxfp4(xs)
+    assert_same(s.reshape(-1, K // 32)[idx], so, "mx scales")
+    assert_same(p.reshape(-1, K // 2)[idx], po, "mx packed")
+    assert_same(y.reshape(-1, K)[idx], oracle.dequantize_mxfp4(po, so, torch.bfloat16), "mx dequant")
+    del p, s, y
+    p, s, g = mxq().quantize_nvfp4(x)
+    y = mxq().dequantize_nvfp4(p, s, g, torch.bfloat16)
+    po, so, go = oracle.quantize_nvfp4(xs)
+    assert_same(g.reshape(-1)[idx], go, "nv row scale")
+    assert_same(s.reshape(-1, K // 16)[idx], so, "nv scales")
+    assert_same(p.reshape(-1, K // 2)[idx], po, "nv packed")
+    assert_same(y.reshape(-1, K)[idx], oracle.dequantize_nvfp4(po, so, go, torch.bfloat16), "nv dequant")
