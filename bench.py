@@ -1,0 +1,237 @@
+"""Throughput of the block-scaled microscaling hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  * the large MoE-expert sweep, bfloat16 [256, 2048, 7168] (about 3.8 G
+    parameters, with 0.1% all-zero, bf16-subnormal and +-1e4-spike 32-column
+    blocks), processed in 36-expert chunks of about 1 GiB: MXFP4 quantize-pack,
+    MXFP4 dequantize to bf16, NVFP4 quantize-pack (per-row scale), NVFP4
+    dequantize to bf16, chunk by chunk;
+  * the cache quantize/dequantize round trip on KV-cache-shaped bf16 tensors:
+    fp8 block 32 [16, 8192, 512], mxfp4 block 32 [16, 8192, 128], nvfp4 block
+    16 [16, 2048, 512].
+`value` is effective GB/s: algorithmic bytes (every input read once plus every
+output written once) of the whole step divided by the step's wall time.
+
+Prints one JSON line.  Also reports, per kernel, its average launch duration
+from HIP events recorded on the launch stream, the roofline of the dominant
+kernel against MI355X's 8 TB/s HBM peak, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "effective GB/s (in+out) for FP4 quant-pack & dequant; % of MI355X HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU-oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--experts", type=int, default=256,
+                    help="experts of the sweep (256 is the full workload)")
+    return ap.parse_args()
+
+
+def bytes_mx(n_elem: int) -> int:
+    # bf16 in (2 B) + packed (1/2 B) + one e8m0 byte per 32
+    return 2 * n_elem + n_elem // 2 + n_elem // 32
+
+
+def bytes_nv(n_elem: int, rows: int) -> int:
+    # bf16 in + packed + one e4m3 byte per 16 + one float32 per row
+    return 2 * n_elem + n_elem // 2 + n_elem // 16 + 4 * rows
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_quantize_pack_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode()); h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"^source_hash:\s*(\S+)", txt, re.M)
+    if not m or m.group(1) != src_hash:
+        return None
+    m = re.search(rf"^{re.escape(kernel)}\s+traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    return float(m.group(1)) if m else None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_quantize_pack_amd as mxq
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- inputs (generated once, resident in HBM) ----------------
+    E, N, K = synth.SHAPES["c5"]
+    E = args.experts
+    chunks = synth.c5_chunks(E)
+    x = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    for cid, e0, ne in chunks:
+        x[e0:e0 + ne] = synth.c5_chunk(cid, ne, device=dev)
+    mx_p = torch.empty((E, N, K // 2), dtype=torch.int8, device=dev)
+    mx_s = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    nv_p = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    nv_s = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
+    nv_g = torch.empty((E, N), dtype=torch.float32, device=dev)
+    y = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    cache_cases = [("c4a", "fp8", 32), ("c4b", "mxfp4", 32), ("c4c", "nvfp4", 16)]
+    cache_in = {c: synth.kv_cache(synth.SHAPES[c], seed=synth.SEEDS[c], device=dev) for c, _, _ in cache_cases}
+    cache_out = {c: torch.empty_like(v) for c, v in cache_in.items()}
+    torch.cuda.synchronize()
+
+    # ---------------- one step: list of (op name, bytes, callable) ----------------
+    plan = []
+    for cid, e0, ne in chunks:
+        sl = slice(e0, e0 + ne)
+        n = ne * N * K
+        xs, ys = x[sl], y[sl]
+        mp, ms, np_, ns, ng = mx_p[sl], mx_s[sl], nv_p[sl], nv_s[sl], nv_g[sl]
+        plan.append(("mxfp4_quant", bytes_mx(n), lambda xs=xs, mp=mp, ms=ms: mxq.mxq_quantize_mxfp4(xs, mp, ms)))
+        plan.append(("mxfp4_dequant", bytes_mx(n), lambda mp=mp, ms=ms, ys=ys: mxq.mxq_dequantize_mxfp4(mp, ms, ys)))
+        plan.append(("nvfp4_quant", bytes_nv(n, ne * N),
+                     lambda xs=xs, np_=np_, ns=ns, ng=ng: mxq.mxq_quantize_nvfp4(xs, np_, ns, ng)))
+        plan.append(("nvfp4_dequant", bytes_nv(n, ne * N),
+                     lambda np_=np_, ns=ns, ng=ng, ys=ys: mxq.mxq_dequantize_nvfp4(np_, ns, ng, ys)))
+    for c, fmt, B in cache_cases:
+        xi, yo = cache_in[c], cache_out[c]
+        plan.append((f"cache_{fmt}", 4 * xi.numel(),
+                     lambda xi=xi, yo=yo, fmt=fmt, B=B: mxq.mxq_quantize_cache(xi, yo, fmt, B)))
+    step_bytes = sum(b for _, b, _ in plan)
+
+    def run_step(events=None):
+        for i, (_, _, fn) in enumerate(plan):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronized on both sides
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in plan] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (wall / args.steps) / 1e9
+
+    # per-kernel averages from the events
+    ops = {}
+    for s in range(args.steps):
+        for i, (name, b, _) in enumerate(plan):
+            t = ev[s][i][0].elapsed_time(ev[s][i][1])
+            o = ops.setdefault(name, {"launches": 0, "bytes": 0, "ms": 0.0})
+            o["launches"] += 1; o["bytes"] += b; o["ms"] += t
+    for name, o in ops.items():
+        o["avg_launch_us"] = round(o["ms"] * 1e3 / o["launches"], 2)
+        o["GBps"] = round(o["bytes"] / (o["ms"] * 1e-3) / 1e9, 1)
+        o["frac_of_peak"] = round(o["GBps"] / PEAK_HBM_GBPS, 4)
+        o["ms"] = round(o["ms"], 3)
+    fp4 = [n for n in ops if not n.startswith("cache")]
+    fp4_bytes = sum(ops[n]["bytes"] for n in fp4)
+    fp4_ms = sum(ops[n]["ms"] for n in fp4)
+    dom = max(ops, key=lambda n: ops[n]["ms"])
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(dom, src_hash)
+    achieved = ops[dom]["GBps"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": traffic,
+                "algorithmic_bytes_per_launch": ops[dom]["bytes"] // ops[dom]["launches"],
+                "avg_launch_us": ops[dom]["avg_launch_us"]}
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "MoE expert sweep bf16 [%d,2048,7168] in 36-expert chunks: MXFP4 + NVFP4 "
+                               "quantize-pack and dequantize to bf16; plus cache QDQ fp8/b32 [16,8192,512], "
+                               "mxfp4/b32 [16,8192,128], nvfp4/b16 [16,2048,512]" % E,
+                   "parallelism": "single GPU", "chunks": len(chunks), "step_bytes": step_bytes},
+        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "fp4_sweep_GBps": round(fp4_bytes / (fp4_ms * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ops": ops,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(x_gpu, budget_s: float):
+    """The CPU oracle, as it is, on whole rows of the same sweep until the time
+    budget is spent; all four weight operations per row batch, one thread."""
+    import torch
+    import oracle
+    K = x_gpu.shape[-1]
+    rows = x_gpu.reshape(-1, K)
+    batch = 256
+    done_rows, secs, nbytes = 0, 0.0, 0
+    start = 0
+    while secs < budget_s and start < rows.shape[0]:
+        xs = rows[start:start + batch].cpu()
+        t = time.perf_counter()
+        p, s = oracle.quantize_mxfp4(xs)
+        oracle.dequantize_mxfp4(p, s, torch.bfloat16)
+        p, s, g = oracle.quantize_nvfp4(xs)
+        oracle.dequantize_nvfp4(p, s, g, torch.bfloat16)
+        secs += time.perf_counter() - t
+        n = xs.numel()
+        nbytes += 2 * bytes_mx(n) + 2 * bytes_nv(n, xs.shape[0])
+        done_rows += xs.shape[0]
+        start += batch * 16   # spread the sample over the tensor
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_rows} rows x 7168 of the sweep (every 16th 256-row batch), "
+                      f"MXFP4+NVFP4 quantize and dequantize, {secs:.1f} s single-threaded"}
+
+
+if __name__ == "__main__":
+    main()
