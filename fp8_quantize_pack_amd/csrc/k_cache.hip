@@ -16,6 +16,14 @@
 // per wavefront), the row's groups are padded to whole lane groups so that a
 // partial last group simply has idle lanes that contribute 0 to its amax.
 // Generic path (anything else): one thread per group, scalar loads.
+//
+// The e2m1 formats round with the gfx950 scaled fp4 converter (round half
+// down; float32 inputs and nvfp4 quotients rounded up to 22 significant bits
+// first, which changes no decision) and decode with the exact fp4 dequantizer;
+// the nvfp4 quotient x / sigma is taken as a binary64 product with the
+// correctly rounded 1 / sigma: x has at most 24 significant bits and sigma 4,
+// so x / sigma is never a float32 decision boundary and lies at least 2^-29
+// (relative) away from each, far beyond the product's 2^-52 error.
 #include "mxq_kernel_common.h"
 #include "mxq_launch.h"
 
@@ -55,8 +63,37 @@ __global__ __launch_bounds__(256) void k_cache_qdq(const void* __restrict__ x,
       a = group_max<G>(a);
       const CacheGroupScale gs = cache_scale(FMT, a);
       float o[8];
+      if constexpr (FMT == FMT_FP8 || DT == DT_F16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = cache_qdq1(FMT, DT == DT_F32, f[i], gs);
+        for (int i = 0; i < 8; ++i) o[i] = cache_qdq1(FMT, DT == DT_F32, f[i], gs);
+      } else {
+        // e2m1 formats: quantize with the scaled fp4 converter (round half
+        // down), decode exactly with the fp4 dequantizer.
+        float q[8];
+        float cvt_scale;
+        if constexpr (FMT == FMT_MXFP4) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q[i] = (DT == DT_F32) ? ceil22(f[i]) : f[i];
+          cvt_scale = gs.s;                         // power of two: x / s inside
+        } else {
+          const double rs = 1.0 / (double)gs.s;     // sigma: an e4m3 value
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f[i] * rs));
+          cvt_scale = 1.0f;
+        }
+        const uint32_t w = e2m1_canonical_zeros(e2m1_pack8_hw(q, cvt_scale));
+        if constexpr (FMT == FMT_MXFP4 && DT == DT_BF16) {
+          if (ok) __builtin_nontemporal_store(e2m1_unpack8_bf16_hw(w, gs.s),
+                                              reinterpret_cast<u32x4*>(y) + rbase + j);
+          continue;
+        } else if constexpr (FMT == FMT_MXFP4) {
+          e2m1_unpack8_f32_hw(w, gs.s, o);
+        } else {
+          e2m1_unpack8_f32_hw(w, 1.0f, o);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = o[i] * gs.s;  // exact
+        }
+      }
       if (ok) st8<DT>(y, rbase + j, o);
     }
   }

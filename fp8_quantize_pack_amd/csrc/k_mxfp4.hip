@@ -13,6 +13,12 @@
 // 256 B (packed) range, and the 4 lanes of a quad own one 32-column block
 // (their amax is combined with two DPP quad permutes).  A tile covers 128
 // blocks, so its 128 scale bytes fill one 128-byte cache line.
+//
+// Rounding and packing use the gfx950 scaled fp4 converts (see
+// mxq_kernel_common.h): the quantizer divides by the block's power-of-two
+// scale and rounds half down; the dequantizer multiplies back exactly.
+// float32 inputs are first rounded up to 22 significant bits (ceil22), which
+// changes no e2m1 decision; bfloat16 and float16 values already fit.
 #include "mxq_kernel_common.h"
 #include "mxq_launch.h"
 
@@ -46,7 +52,11 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
       a = group_max<4>(a);                      // amax of the 32-column block
       const uint32_t sb = mxfp4_scale_byte(a);  // e8m0 byte
-      const uint32_t word = mxfp4_quant8(f, sb, DT == DT_F32);
+      if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = ceil22(f[i]);
+      }
+      const uint32_t word = e2m1_pack8_hw(f, e8m0_as_scale(sb));
       if (c < nchunks) {
         __builtin_nontemporal_store(word, packed + c);
         if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sb;
@@ -75,9 +85,28 @@ __global__ __launch_bounds__(256) void k_mxfp4_dequant(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t c = c0 + u * kWave;
-      float f[8];
-      mxfp4_dequant8(w[u], sb[u], f);
-      if (c < nchunks) st8<DT>(y, c, f);
+      if constexpr (DT == DT_F16) {
+        float f[8];
+        mxfp4_dequant8(w[u], sb[u], f);
+        if (c < nchunks) st8<DT>(y, c, f);
+      } else {
+        const uint32_t wc = e2m1_canonical_zeros(w[u]);
+        const float scale = e8m0_as_scale(sb[u]);
+        const bool nan_scale = sb[u] == 255u;             // e8m0 NaN
+        if constexpr (DT == DT_BF16) {
+          u32x4 o = e2m1_unpack8_bf16_hw(wc, scale);
+          if (nan_scale) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+          if (c < nchunks) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(y) + c);
+        } else {
+          float f[8];
+          e2m1_unpack8_f32_hw(wc, scale, f);
+          if (nan_scale) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = bitsf(0x7FC00000u);
+          }
+          if (c < nchunks) st8<DT>(y, c, f);
+        }
+      }
     }
   }
 }

@@ -80,6 +80,8 @@ __device__ __forceinline__ void unpack8<DT_F32>(const Raw8<DT_F32>& r, float f[8
   f[4] = bitsf(r.b.x); f[5] = bitsf(r.b.y); f[6] = bitsf(r.b.z); f[7] = bitsf(r.b.w);
 }
 
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi);
+
 // Round 8 float32 values to DT (round to nearest even) and store them.
 template <int DT>
 __device__ __forceinline__ void st8(void* base, int64_t c, const float f[8]);
@@ -92,11 +94,8 @@ __device__ __forceinline__ void st8<DT_F32>(void* base, int64_t c, const float f
 }
 template <>
 __device__ __forceinline__ void st8<DT_BF16>(void* base, int64_t c, const float f[8]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = f32_to_bf16_rne(f[2 * i]) | (f32_to_bf16_rne(f[2 * i + 1]) << 16);
-  __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
+  __builtin_nontemporal_store(u32x4{bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]),
+                                    bf16x2_rne(f[4], f[5]), bf16x2_rne(f[6], f[7])},
                               reinterpret_cast<u32x4*>(base) + c);
 }
 template <>
@@ -107,6 +106,94 @@ __device__ __forceinline__ void st8<DT_F16>(void* base, int64_t c, const float f
     w[i] = f32_to_f16_rne(f[2 * i]) | (f32_to_f16_rne(f[2 * i + 1]) << 16);
   __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
                               reinterpret_cast<u32x4*>(base) + c);
+}
+
+// ------------------------------------------------------------------ gfx950 converts
+// The CDNA4 scaled fp4 converts.  Their scale operand is read as a power of
+// two taken from the float's exponent field (an e8m0 byte b is passed as the
+// float with bit pattern b << 23; byte 0 means 2^-127).  Quantizing converts
+// divide by that power of two, dequantizing converts multiply by it.
+// Measured properties this file relies on (exhaustively over every bfloat16
+// value under every e8m0 scale, and over float32 values adjacent to every
+// e2m1 midpoint):
+//  * the stochastic-rounding quantizer adds a fixed "random" operand below
+//    the kept mantissa bit and truncates; with the operands below it rounds
+//    half down, i.e. to the nearest e2m1 value with ties to the smaller
+//    magnitude, for operands with at most 22 significant bits (see ceil22).
+//    The two elements of a pair read different bits of the operand, so each
+//    pair is converted twice and the correct nibble of each kept;
+//  * the sign nibble bit is the operand's sign bit (also for zeros);
+//  * the dequantizers are exact, including subnormal results, except that
+//    code 8 decodes to -0.0 (callers clear those sign bits first).
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kSrHalfDownEven = 0x7FFFFC00u;   // element 0 of a pair
+constexpr uint32_t kSrHalfDownOdd = 0x3FFFFF00u;    // element 1 of a pair
+
+__device__ __forceinline__ float e8m0_as_scale(uint32_t b) { return bitsf(b << 23); }
+
+// One pair through the stochastic-rounding quantizer, result in byte 0.
+// (The builtin's "old" operand is not tied to its result by the compiler, so
+// the byte-select forms cannot be chained; every pair is converted into byte
+// 0 of a fresh value and the bytes are assembled with v_perm_b32.)
+__device__ __forceinline__ uint32_t sr_fp4_pair(float a, float b, uint32_t seed, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{a, b}, seed, scale, 0);
+}
+
+// Byte 0 of each of p0..p3 -> bytes 0..3 of the result.
+__device__ __forceinline__ uint32_t gather_byte0(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3) {
+  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);   // [p0.b0, p1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);   // [0, 0, p2.b0, p3.b0]
+  return lo | hi;
+}
+
+// 8 values (at most 22 significant bits each) -> 8 e2m1 codes, element i in
+// nibble i, each value first divided by the power of two `scale`.
+__device__ __forceinline__ uint32_t e2m1_pack8_hw(const float f[8], float scale) {
+  const uint32_t e = gather_byte0(sr_fp4_pair(f[0], f[1], kSrHalfDownEven, scale),
+                                  sr_fp4_pair(f[2], f[3], kSrHalfDownEven, scale),
+                                  sr_fp4_pair(f[4], f[5], kSrHalfDownEven, scale),
+                                  sr_fp4_pair(f[6], f[7], kSrHalfDownEven, scale));
+  const uint32_t o = gather_byte0(sr_fp4_pair(f[0], f[1], kSrHalfDownOdd, scale),
+                                  sr_fp4_pair(f[2], f[3], kSrHalfDownOdd, scale),
+                                  sr_fp4_pair(f[4], f[5], kSrHalfDownOdd, scale),
+                                  sr_fp4_pair(f[6], f[7], kSrHalfDownOdd, scale));
+  return o ^ ((e ^ o) & 0x0F0F0F0Fu);          // low nibbles from e, high from o
+}
+
+// Clear the sign bit of every zero-magnitude nibble (code 8 -> 0), so that it
+// decodes to +0.0 as the e2m1 table prescribes.
+__device__ __forceinline__ uint32_t e2m1_canonical_zeros(uint32_t w) {
+  const uint32_t nz = ((w & 0x77777777u) + 0x77777777u) & 0x88888888u;
+  return w & (nz | 0x77777777u);
+}
+
+// 8 codes -> 8 float32 values e2m1 * scale (exact).  w must be canonical.
+__device__ __forceinline__ void e2m1_unpack8_f32_hw(uint32_t w, float scale, float out[8]) {
+  f32x2 v;
+  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0); out[0] = v.x; out[1] = v.y;
+  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1); out[2] = v.x; out[3] = v.y;
+  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2); out[4] = v.x; out[5] = v.y;
+  v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3); out[6] = v.x; out[7] = v.y;
+}
+
+// 8 codes -> 8 bfloat16 values (4 packed dwords) e2m1 * scale (exact).
+__device__ __forceinline__ u32x4 e2m1_unpack8_bf16_hw(uint32_t w, float scale) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return r;
+}
+
+// Two float32 -> packed bfloat16 pair, round to nearest even (v_cvt_pk_bf16_f32,
+// IEEE with subnormals; measured bit-exact).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
 // ------------------------------------------------------------------ reductions

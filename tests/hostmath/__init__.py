@@ -39,8 +39,12 @@ def lib():
         L.hm_quantize_nvfp4.argtypes = [vp, i32, i64, i64, i32, vp, i64, vp, vp, vp]
         L.hm_dequantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, vp, i32]
         L.hm_quantize_cache.argtypes = [vp, vp, i32, i64, i64, i32, i64]
-        for f in ("hm_e4m3_encode_pos", "hm_e4m3_round_value", "hm_pow2_ceil", "hm_bf16_rne"):
+        for f in ("hm_e4m3_encode_pos", "hm_e4m3_round_value", "hm_pow2_ceil", "hm_bf16_rne", "hm_f16_rne"):
             getattr(L, f).argtypes = [vp, i64, vp]
+        L.hm_nv_division_stress.argtypes = [i64, ctypes.c_uint64, i32]
+        L.hm_nv_division_stress.restype = i64
+        L.hm_ceil22_check.argtypes = []
+        L.hm_ceil22_check.restype = i64
         _lib = L
     return _lib
 

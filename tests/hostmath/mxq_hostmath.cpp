@@ -64,14 +64,15 @@ void hm_quantize_nvfp4(const void* x, int dt, int64_t rows, int64_t K, int mode,
     const float g = mode == 1 ? given[r * given_stride]
                   : mode == 2 ? tensor_amax / 2688.0f : amax / 2688.0f;
     row_scale[r] = g;
+    const double rg = 1.0 / (double)g;
     for (int64_t b = 0; b < K / 16; ++b) {
       float f[16];
       float a = 0.0f;
       for (int i = 0; i < 16; ++i) { f[i] = ld(x, dt, r * K + 16 * b + i); a = fmaxf(a, fabsf(f[i])); }
       float den;
-      scales[r * (K / 16) + b] = (uint8_t)nvfp4_block_scale(a, g, &den);
+      scales[r * (K / 16) + b] = (uint8_t)nvfp4_block_scale(a, g, rg, &den);
       for (int c = 0; c < 2; ++c)
-        put_word(packed + r * (K / 2) + 8 * b + 4 * c, nvfp4_quant8(f + 8 * c, den));
+        put_word(packed + r * (K / 2) + 8 * b + 4 * c, nvfp4_quant8(f + 8 * c, 1.0 / (double)den));
     }
   }
 }
@@ -115,3 +116,63 @@ void hm_bf16_rne(const float* v, int64_t n, uint16_t* out) {
 }
 
 }  // extern "C"
+
+extern "C" void hm_f16_rne(const float* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint16_t)mxq::f32_to_f16_rne(v[i]);
+}
+
+// Stress of the NVFP4 division shortcuts against IEEE float32 division on the
+// host: random (x, den) pairs plus pairs built to sit on or next to an e2m1
+// rounding boundary.  Returns the number of disagreements.
+static uint64_t splitmix(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+extern "C" int64_t hm_nv_division_stress(int64_t n, uint64_t seed, int wide) {
+  static const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  int64_t bad = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const uint64_t r = splitmix(seed);
+    // den: random float32 in [2^-40, 2^20], or sigma * 2^k (exact e4m3 times pow2)
+    float den;
+    if (r & 1) den = bitsf((uint32_t)(((r >> 8) % (60u << 23)) + (87u << 23)));
+    else den = e4m3_decode_pos(1 + (uint32_t)((r >> 8) % 126)) * bitsf((uint32_t)((100 + (r >> 20) % 40) << 23));
+    float x;
+    const int kind = (int)((r >> 40) % 4);
+    const float m = mids[(r >> 44) % 7];
+    float t = m * den;                                 // near a midpoint
+    if (kind == 0) x = bitsf((uint32_t)(splitmix(seed) % 0x7F7FFFFFu)) ;   // random
+    else x = t;
+    if (!wide) x = bitsf(fbits(x) & 0xFFFF0000u);      // bf16 input
+    if (kind == 2) x = bitsf(fbits(x) + (wide ? 1u : 0x10000u));
+    if (kind == 3) x = bitsf(fbits(x) - (wide ? 1u : 0x10000u));
+    if (!(x == x) || x > 3e38f) continue;
+    const float q_ref = fabsf(x) / den;
+    const uint32_t want = e2m1_mag_f32(q_ref == q_ref ? q_ref : 0.0f);
+    float q = (float)((double)fabsf(x) * (1.0 / (double)den));
+    q = (q == q) ? q : 0.0f;
+    if (e2m1_mag_f32(q) != want) ++bad;
+    // block-scale chain: (a / 6) / g
+    const float g = den;
+    const float u_ref = (fabsf(x) / 6.0f) / g;
+    const float u = (float)((double)div6_rn(fabsf(x)) * (1.0 / (double)g));
+    if (fbits(u) != fbits(u_ref) && u_ref >= 1.17549435e-38f) ++bad;
+  }
+  return bad;
+}
+
+// Every non-negative float32 below 16 (and +inf): the e2m1 code of ceil22(q)
+// equals the code of q.  Returns the number of disagreements.
+extern "C" int64_t hm_ceil22_check(void) {
+  int64_t bad = 0;
+  for (uint32_t b = 0; b <= 0x41800000u; ++b) {
+    const float q = bitsf(b);
+    if (e2m1_mag_f32(ceil22(q)) != e2m1_mag_f32(q)) ++bad;
+    const float nq = ceil22(-q);                     // sign kept, same magnitude rounding
+    if (!signbit(nq) || e2m1_mag_f32(fabsf(nq)) != e2m1_mag_f32(q)) ++bad;
+  }
+  if (e2m1_mag_f32(ceil22(bitsf(0x7F800000u))) != 7u) ++bad;
+  return bad;
+}

@@ -167,12 +167,74 @@ def test_mxfp4_exhaustive_bf16_under_every_scale():
         vals = np.concatenate([vals, np.zeros((-vals.size) % 31, np.float32)]).reshape(-1, 31)
         rows.append(np.concatenate([np.full((vals.shape[0], 1), anchor, np.float32), vals], 1))
     x = torch.from_numpy(np.concatenate(rows)).to(torch.bfloat16)
+    # second layout: the 31 values shifted by one column, so that every value
+    # also sits in the other position of its byte (odd <-> even column)
+    x2 = torch.cat([x[:, :1], x[:, 2:], x[:, 1:2]], 1)
+    for xin in (x, x2):
+        po, so = oracle.quantize_mxfp4(xin)
+        p, s = gpu_quantize_mxfp4(xin.to(DEV))
+        assert_same(s, so, "scales")
+        assert_same(p, po, "packed")
+        assert_same(gpu_dequantize_mxfp4(p, s, torch.bfloat16),
+                    oracle.dequantize_mxfp4(po, so, torch.bfloat16), "dequant")
+
+
+def test_mxfp4_fp32_planted_midpoints():
+    """float32 inputs on, just below and just above every e2m1 midpoint of
+    their block's scale (24-bit significands), both byte positions."""
+    say("mxfp4 fp32 planted midpoints")
+    rng = np.random.default_rng(1)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    n = 4096
+    sc = np.exp2(rng.integers(-120, 120, n)).astype(np.float32)
+    blk = np.zeros((n, 32), np.float32)
+    blk[:, 0] = 6.0 * sc
+    for j in range(1, 32):
+        m = mids[rng.integers(0, 7, n)]
+        d = rng.integers(-3, 4, n)
+        v = (m.view(np.uint32).astype(np.int64) + d).astype(np.uint32).view(np.float32)
+        blk[:, j] = v * sc * np.where(rng.random(n) < 0.5, -1, 1)
+    x = torch.from_numpy(blk)
     po, so = oracle.quantize_mxfp4(x)
     p, s = gpu_quantize_mxfp4(x.to(DEV))
     assert_same(s, so, "scales")
     assert_same(p, po, "packed")
-    assert_same(gpu_dequantize_mxfp4(p, s, torch.bfloat16),
-                oracle.dequantize_mxfp4(po, so, torch.bfloat16), "dequant")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_nvfp4_quotients_hugging_decision_boundaries(dtype):
+    """Elements placed at m * den and at its neighbouring representable values
+    for every e2m1 midpoint m, with arbitrary (given) row scales and power-of-two
+    ones (exact ties)."""
+    say("nvfp4 boundary-hugging quotients", dtype)
+    rng = np.random.default_rng(17)
+    R, K = 512, 256
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    g = np.where(rng.random(R) < 0.5, np.exp2(rng.integers(-14, -4, R)), rng.random(R) * 1e-3 + 1e-6).astype(np.float32)
+    x = np.zeros((R, K), np.float32)
+    for r in range(R):
+        for b in range(K // 16):
+            sigma = np.float32(2.0 ** rng.integers(-3, 6) * (1 + rng.integers(0, 8) / 8))
+            den = np.float32(sigma * g[r])
+            blk = np.empty(16, np.float32)
+            blk[0] = np.float32(6.0 * den)            # block amax 6 * den: block scale = sigma
+            m = mids[rng.integers(0, 7, 15)]
+            t = (m * den).astype(np.float32)
+            step = rng.integers(-2, 3, 15)
+            if dtype == torch.bfloat16:
+                tb = torch.from_numpy(t).to(torch.bfloat16).view(torch.int16).numpy().astype(np.int32)
+                tb = (tb + step).astype(np.int16)
+                t = torch.from_numpy(tb).view(torch.bfloat16).float().numpy()
+            else:
+                t = (t.view(np.uint32).astype(np.int64) + step).astype(np.uint32).view(np.float32)
+            blk[1:] = t * np.where(rng.random(15) < 0.5, -1, 1)
+            x[r, 16 * b:16 * b + 16] = blk
+    xt = torch.from_numpy(x).to(dtype)
+    gt = torch.from_numpy(g)
+    po, so, go = oracle.quantize_nvfp4(xt, mode="given", given=gt)
+    p, s, gg = gpu_quantize_nvfp4(xt.to(DEV), mode="given", given=gt)
+    assert_same(s, so, "scales")
+    assert_same(p, po, "packed")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])

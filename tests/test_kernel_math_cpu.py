@@ -233,3 +233,29 @@ def test_pow2_ceil_matches_oracle_on_all_exponents():
     got = hm.apply("hm_pow2_ceil", torch.from_numpy(v), torch.float32).numpy()
     want = np.array([oracle.pow2_ceil(float(t)) for t in v[:20000]], np.float32)
     assert np.array_equal(got[:20000], want)
+
+
+def test_f16_rounding_against_torch():
+    rng = np.random.default_rng(12)
+    bits = np.concatenate([rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32),
+                           # every float32 with an exponent in the float16 range and 12 low bits
+                           ((np.arange(0x33000000 >> 12, 0x47800000 >> 12, dtype=np.uint32) << 12)
+                            | rng.integers(0, 1 << 12, (0x47800000 >> 12) - (0x33000000 >> 12), dtype=np.uint32)),
+                           np.array([0x80000000, 0, 0x33000000, 0x33000001, 0x477FEFFF, 0x477FF000], np.uint32)])
+    f = torch.from_numpy(bits.view(np.float32))
+    f = torch.cat([f, -f])
+    f = f[~torch.isnan(f)]
+    got = hm.apply("hm_f16_rne", f, torch.int16)
+    assert torch.equal(got, f.to(torch.float16).view(torch.int16))
+
+
+@pytest.mark.parametrize("wide", [0, 1])
+def test_nvfp4_binary64_division_shortcut_stress(wide):
+    """The kernels replace float32 divisions by binary64 products; on random
+    and boundary-hugging pairs the decisions must match IEEE float32 division."""
+    assert hm.lib().hm_nv_division_stress(3_000_000, 1234 + wide, wide) == 0
+
+
+def test_rounding_up_to_22_bits_keeps_every_e2m1_decision():
+    """Exhaustive over all float32 magnitudes below 16 (about 1.1e9 values)."""
+    assert hm.lib().hm_ceil22_check() == 0
