@@ -41,12 +41,12 @@ _STATUS = {
 }
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with "
+            f"{path} is missing: build it with "
             "`python -m fp8_quantize_pack_amd.build` (hipcc, gfx950)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.mxq_quantize_mxfp4.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     L.mxq_dequantize_mxfp4.argtypes = [vp, vp, i64, i64, vp, i32, vp]

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void k_cache_qdq(const void* __restrict__ x,
         }
         const uint32_t w = e2m1_canonical_zeros(e2m1_pack8_hw(q, cvt_scale));
         if constexpr (FMT == FMT_MXFP4 && DT == DT_BF16) {
-          if (ok) __builtin_nontemporal_store(e2m1_unpack8_bf16_hw(w, gs.s),
+          if (ok) stream_st(e2m1_unpack8_bf16_hw(w, gs.s),
                                               reinterpret_cast<u32x4*>(y) + rbase + j);
           continue;
         } else if constexpr (FMT == FMT_MXFP4) {
@@ -141,7 +141,7 @@ static hipError_t launch_fast(const void* x, void* y, const CacheGeom& geo,
                               int B, hipStream_t s) {
   const int64_t rows_per_wave = kWave / geo.lpr;
   const int64_t waves = (geo.rows + rows_per_wave - 1) / rows_per_wave;
-  const int64_t max_blocks = 256 * 8;
+  const int64_t max_blocks = kCacheGridBlocks;
   int64_t b = (waves + 3) / 4;
   const dim3 grid((unsigned)(b < max_blocks ? (b > 0 ? b : 1) : max_blocks)), block(256);
   switch (B) {

@@ -24,7 +24,10 @@
 
 namespace mxq {
 
-constexpr int kUnroll = 8;
+#ifndef MXQ_MX_UNROLL
+#define MXQ_MX_UNROLL 8
+#endif
+constexpr int kUnroll = MXQ_MX_UNROLL;
 constexpr int kTileChunks = kUnroll * kWave;   // 512 chunks = 4096 elements
 
 template <int DT>
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(
       }
       const uint32_t word = e2m1_pack8_hw(f, e8m0_as_scale(sb));
       if (c < nchunks) {
-        __builtin_nontemporal_store(word, packed + c);
+        stream_st(word, packed + c);
         if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sb;
       }
     }
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(256) void k_mxfp4_dequant(
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t c = c0 + u * kWave;
       const bool ok = c < nchunks;
-      w[u] = ok ? __builtin_nontemporal_load(packed + c) : 0u;
+      w[u] = ok ? stream_ld(packed + c) : 0u;
       sb[u] = ok ? (uint32_t)scales[c >> 2] : 0u;
     }
 #pragma unroll
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256) void k_mxfp4_dequant(
         if constexpr (DT == DT_BF16) {
           u32x4 o = e2m1_unpack8_bf16_hw(wc, scale);
           if (nan_scale) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-          if (c < nchunks) __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(y) + c);
+          if (c < nchunks) stream_st(o, reinterpret_cast<u32x4*>(y) + c);
         } else {
           float f[8];
           e2m1_unpack8_f32_hw(wc, scale, f);
@@ -112,9 +115,8 @@ __global__ __launch_bounds__(256) void k_mxfp4_dequant(
 }
 
 static int grid_for(int64_t ntiles) {
-  // Enough resident waves to cover latency on 256 CUs; the loop strides the
-  // rest.  4 waves per workgroup.
-  const int64_t max_blocks = 256 * 8;
+  // One tile per wave, 4 waves per workgroup, up to the grid cap.
+  const int64_t max_blocks = kMaxGridBlocks;
   int64_t b = (ntiles + 3) / 4;
   return (int)(b < max_blocks ? (b > 0 ? b : 1) : max_blocks);
 }

@@ -8,14 +8,21 @@
 //   code        = round_to_e2m1(x / (block scale * g))
 //   decode      = e2m1 * e4m3 * g in float32, then one rounding to dtype.
 //
-// Layout of the work.  One lane owns one 16-column block at a time (32 bytes
-// of bfloat16 in, 8 bytes of codes and one scale byte out), so the block amax
-// and the block scale need no lane exchange.  A row is owned by LPR lanes (a
-// power of two, 64 once the row has 64 blocks or more), i.e. 64/LPR rows per
-// wavefront; lane `sub` owns the blocks sub, sub + LPR, ...  With NIT > 0 the
-// whole row stays in registers between the row-amax reduction and the
+// Layout of the work.  Rows of 64 blocks or more are cut into segments of 64
+// blocks (1024 elements).  A wavefront reads a segment with two loads that are
+// each contiguous over the wave: lane L takes chunks L and 64 + L (8 elements
+// each), i.e. one half of blocks L/2 and 32 + L/2, whose other halves sit in
+// lane L ^ 1.  The pair combines its half-block maxima with one DPP swap; the
+// even lane derives the scale of block L/2, the odd lane that of block
+// 32 + L/2, and one more swap hands each lane both reciprocals -- so a wave
+// still computes one scale per lane for 1024 elements.  Codes leave as one
+// dword per lane and instruction, contiguous again.  A row is owned by WPR
+// waves of the workgroup (segments w, w + WPR, ... go to wave w), which
+// combine their row maxima through LDS; with NIT > 0 every wave keeps its
+// NIT segments in registers between the row-amax reduction and the
 // quantization (HBM is read once); NIT == 0 is the fallback for very long
-// rows, which reads the row twice.
+// rows, which reads the row twice.  Rows of fewer than 64 blocks take one
+// block per lane, several rows per wave.
 //
 // Exactness of the element step: q = RN(x / den) is needed only through the
 // e2m1 decisions q > m.  The kernel forms the binary64 product x * (1 / den)
@@ -31,24 +38,8 @@ namespace mxq {
 constexpr float kGlobalDiv = 2688.0f;         // E2M1_MAX * E4M3_MAX
 constexpr double kHugeRecip = 0x1p800;        // stands in for 1 / 0 (see below)
 
-struct NvRowGeom {
-  int64_t rows;
-  int64_t bpr;      // 16-column blocks per row = K / 16
-  int lpr;          // lanes per row
-  int niter;        // block iterations per lane = ceil(bpr / lpr)
-};
-
-// 16 elements (one block) as two 8-element chunks.
-template <int DT> struct Raw16 { Raw8<DT> lo, hi; };
-
-template <int DT>
-__device__ __forceinline__ Raw16<DT> ld16(const void* x, int64_t blk) {
-  return Raw16<DT>{ld8<DT>(x, 2 * blk), ld8<DT>(x, 2 * blk + 1)};
-}
-template <int DT>
-__device__ __forceinline__ Raw16<DT> zero16() {
-  return Raw16<DT>{zero8<DT>(), zero8<DT>()};
-}
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float nv_row_scale(int mode, float row_amax,
                                               const float* given,
@@ -59,107 +50,251 @@ __device__ __forceinline__ float nv_row_scale(int mode, float row_amax,
   return row_amax / kGlobalDiv;
 }
 
+// Magnitude maximum of 8 elements as a bit pattern that orders like the
+// value: bfloat16 and float16 magnitudes order like their 15-bit patterns, so
+// the maximum is taken on the raw data with packed 16-bit integer maxima (two
+// elements per instruction); float32 uses the float maximum.
 template <int DT>
-__device__ __forceinline__ float amax16(const Raw16<DT>& r) {
-  float f[8], h[8];
-  unpack8<DT>(r.lo, f);
-  unpack8<DT>(r.hi, h);
-  float a = 0.0f;
+__device__ __forceinline__ uint32_t amax8_bits(const Raw8<DT>& r) {
+  if constexpr (DT == DT_F32) {
+    float f[8];
+    unpack8<DT>(r, f);
+    float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fmaxf(fabsf(f[i]), fabsf(h[i])));
-  return a;
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+    return fbits(a);
+  } else {
+    const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+    u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    return m.x > m.y ? m.x : m.y;
+  }
 }
 
-// Quantize one block: returns the 16 codes (two words) and the scale byte.
 template <int DT>
-__device__ __forceinline__ void nv_quant_block(const Raw16<DT>& r, float g, double rg,
-                                               uint32_t& w0, uint32_t& w1, uint32_t& sb) {
-  float f[8], h[8];
-  unpack8<DT>(r.lo, f);
-  unpack8<DT>(r.hi, h);
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fmaxf(fabsf(f[i]), fabsf(h[i])));
+__device__ __forceinline__ float amax_from_bits(uint32_t b) {
+  if constexpr (DT == DT_F32) return bitsf(b);
+  else if constexpr (DT == DT_BF16) return bitsf(b << 16);
+  else return f16_to_f32(b);
+}
+
+// Scale byte, and |1 / den| for den = e4m3(a / 6 / g) * g, of a block with
+// amax `a`.  1 / den is correctly rounded in binary64.  den == 0 (only with
+// g == 0 or a tiny given g) makes every non-zero element saturate and keeps
+// 0 / 0 at code 0, as the float32 quotient would (inf -> code 7, NaN -> code
+// 0); den == inf gives 0 (every finite element to code 0).  The magnitude is
+// taken because a code's sign is its element's, whatever the sign of g.
+constexpr int kClassZeroInf = (1 << 2) | (1 << 5) | (1 << 6) | (1 << 9);   // -inf -0 +0 +inf
+
+__device__ __forceinline__ double nv_block_recip(float a, float g, double rg, uint32_t& sb) {
   float den;
   sb = nvfp4_block_scale(a, g, rg, &den);
-  // 1 / den, correctly rounded; den == 0 (only with g == 0) makes every
-  // non-zero element saturate and keeps 0 / 0 at code 0, as the float32
-  // quotient would (inf -> code 7, NaN -> code 0).
-  const double rden = (den == 0.0f) ? kHugeRecip : 1.0 / (double)den;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    f[i] = ceil22((float)((double)f[i] * rden));
-    h[i] = ceil22((float)((double)h[i] * rden));
-  }
-  w0 = e2m1_pack8_hw(f, 1.0f);
-  w1 = e2m1_pack8_hw(h, 1.0f);
+  double r = recip64((double)den);
+  if (__builtin_amdgcn_classf(den, kClassZeroInf)) r = (den == 0.0f) ? kHugeRecip : 0.0;
+  return fabs(r);
 }
 
-template <int DT, int NIT>
-__global__ __launch_bounds__(256) void k_nvfp4_quant(
-    const void* __restrict__ x, NvRowGeom geo, int mode,
+// The same for a row scale g in [2^-100, 2^100]: den = sigma * g then lies in
+// [2^-109, 2^109], finite, non-zero and positive, so none of the cases above
+// arises.
+__device__ __forceinline__ double nv_block_recip_normal(float a, float g, double rg, uint32_t& sb) {
+  float den;
+  sb = nvfp4_block_scale(a, g, rg, &den);
+  return recip64((double)den);
+}
+
+__device__ __forceinline__ bool nv_g_normal(float g) {
+  return g >= 0x1p-100f && g <= 0x1p100f;      // false for NaN
+}
+
+// 8 codes (one dword) of a chunk, given 1 / den of its block.
+template <int DT>
+__device__ __forceinline__ uint32_t nv_codes8(const Raw8<DT>& r, double rden) {
+  float f[8];
+  unpack8<DT>(r, f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = ceil22((float)((double)f[i] * rden));
+  return e2m1_pack8_hw(f, 1.0f);
+}
+
+// Value of lane L ^ 1 (DPP quad_perm [1,0,3,2]; every lane has a source).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ double pair_swap(double d) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, d);
+  const uint64_t lo = pair_swap((uint32_t)u), hi = pair_swap((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+struct NvSegGeom {
+  int64_t rows;
+  int64_t bpr;      // 16-column blocks per row = K / 16
+  int64_t cpr;      // 8-column chunks per row = 2 * bpr
+  int nseg;         // 64-block segments per row = ceil(bpr / 64)
+};
+
+// One segment's two chunks of this lane (zero outside the row).
+template <int DT>
+struct SegChunks { Raw8<DT> c0, c1; };
+
+// With FULL (every segment of a row has 64 blocks) the guards depend only on
+// the row and the segment, which are uniform over the wave.
+template <int DT, bool FULL>
+__device__ __forceinline__ SegChunks<DT> seg_load(const void* x, const NvSegGeom& geo,
+                                                  bool row_ok, int64_t cbase, int seg, int lane) {
+  const int64_t ch0 = (int64_t)seg * 128 + lane;       // chunk index within the row
+  const bool ok0 = FULL ? (row_ok && seg < geo.nseg) : (row_ok && ch0 < geo.cpr);
+  const bool ok1 = FULL ? ok0 : (row_ok && ch0 + 64 < geo.cpr);
+  SegChunks<DT> c;
+  c.c0 = ok0 ? ld8<DT>(x, cbase + ch0) : zero8<DT>();
+  c.c1 = ok1 ? ld8<DT>(x, cbase + ch0 + 64) : zero8<DT>();
+  return c;
+}
+
+// Quantize one loaded segment: block maxima from the pair, one scale per lane,
+// codes of both chunks, stores.
+template <int DT, bool FULL, bool NORMAL>
+__device__ __forceinline__ void seg_quant(const SegChunks<DT>& c, const NvSegGeom& geo,
+                                          bool row_ok, int64_t row, int seg, int lane,
+                                          float g, double rg, uint32_t* __restrict__ packed,
+                                          uint8_t* __restrict__ scales) {
+  uint32_t p0 = amax8_bits<DT>(c.c0), p1 = amax8_bits<DT>(c.c1);
+  p0 = max(p0, pair_swap(p0));                          // block of chunk 0
+  p1 = max(p1, pair_swap(p1));                          // block of chunk 1
+  const bool odd = lane & 1;
+  uint32_t sb;
+  const float a = amax_from_bits<DT>(odd ? p1 : p0);
+  const double mine = NORMAL ? nv_block_recip_normal(a, g, rg, sb) : nv_block_recip(a, g, rg, sb);
+  const double other = pair_swap(mine);
+  const double r0 = odd ? other : mine, r1 = odd ? mine : other;
+  const uint32_t w0 = nv_codes8<DT>(c.c0, r0);
+  const uint32_t w1 = nv_codes8<DT>(c.c1, r1);
+  const int64_t ch0 = (int64_t)seg * 128 + lane;
+  const int64_t cbase = row * geo.cpr;
+  const int64_t blk = (int64_t)seg * 64 + (odd ? 32 : 0) + (lane >> 1);
+  const bool ok0 = FULL ? (row_ok && seg < geo.nseg) : (row_ok && ch0 < geo.cpr);
+  const bool ok1 = FULL ? ok0 : (row_ok && ch0 + 64 < geo.cpr);
+  const bool okb = FULL ? ok0 : (row_ok && blk < geo.bpr);
+  if (ok0) stream_st(w0, packed + cbase + ch0);
+  if (ok1) stream_st(w1, packed + cbase + ch0 + 64);
+  if (okb) scales[row * geo.bpr + blk] = (uint8_t)sb;
+}
+
+template <int DT, int NIT, int WPR, bool FULL>
+__global__ __launch_bounds__(256) void k_nvfp4_quant_seg(
+    const void* __restrict__ x, NvSegGeom geo, int mode,
     const float* __restrict__ given, int64_t given_stride,
-    const uint32_t* __restrict__ tensor_amax, uint2* __restrict__ packed,
+    const uint32_t* __restrict__ tensor_amax, uint32_t* __restrict__ packed,
     uint8_t* __restrict__ scales, float* __restrict__ row_scale) {
+  __shared__ uint32_t part[2][4];              // partial row maxima, double-buffered
   const int lane = threadIdx.x & 63;
-  const int sub = lane & (geo.lpr - 1);
-  const int rows_per_wave = kWave / geo.lpr;
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int64_t ngroups = (geo.rows + rows_per_wave - 1) / rows_per_wave;
-  for (int64_t wg = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-       wg < ngroups; wg += nwaves) {
-    const int64_t row = wg * rows_per_wave + lane / geo.lpr;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+  const int wir = wave % WPR;                  // wave within its row
+  constexpr int rows_per_block = 4 / WPR;
+  const int64_t ngroups = (geo.rows + rows_per_block - 1) / rows_per_block;
+  int buf = 0;
+  for (int64_t bg = blockIdx.x; bg < ngroups; bg += gridDim.x) {
+    const int64_t row = bg * rows_per_block + wave / WPR;
     const bool row_ok = row < geo.rows;
-    const int64_t rbase = row * geo.bpr;
+    const int64_t cbase = row * geo.cpr;
+    SegChunks<DT> c[NIT > 0 ? NIT : 1];
+    float amax = 0.0f;
     if constexpr (NIT > 0) {
-      Raw16<DT> r[NIT];
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int64_t j = sub + (int64_t)it * geo.lpr;
-        r[it] = (row_ok && j < geo.bpr) ? ld16<DT>(x, rbase + j) : zero16<DT>();
-      }
-      float amax = 0.0f;
+      for (int it = 0; it < NIT; ++it) c[it] = seg_load<DT, FULL>(x, geo, row_ok, cbase, wir + it * WPR, lane);
       if (mode == 0) {
+        uint32_t m = 0;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) amax = fmaxf(amax, amax16<DT>(r[it]));
-        amax = group_max_rt(amax, geo.lpr);
-      }
-      const float g = row_ok ? nv_row_scale(mode, amax, given, given_stride, row, tensor_amax) : 1.0f;
-      const double rg = 1.0 / (double)g;
-      if (row_ok && sub == 0) row_scale[row] = g;
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int64_t j = sub + (int64_t)it * geo.lpr;
-        if (row_ok && j < geo.bpr) {
-          uint32_t w0, w1, sb;
-          nv_quant_block<DT>(r[it], g, rg, w0, w1, sb);
-          __builtin_nontemporal_store(w0, &packed[rbase + j].x);
-          __builtin_nontemporal_store(w1, &packed[rbase + j].y);
-          scales[rbase + j] = (uint8_t)sb;
-        }
+        for (int it = 0; it < NIT; ++it) m = max(m, max(amax8_bits<DT>(c[it].c0), amax8_bits<DT>(c[it].c1)));
+        amax = amax_from_bits<DT>(m);
       }
     } else {
-      float amax = 0.0f;
       if (mode == 0) {
-        for (int it = 0; it < geo.niter; ++it) {
-          const int64_t j = sub + (int64_t)it * geo.lpr;
-          if (row_ok && j < geo.bpr) amax = fmaxf(amax, amax16<DT>(ld16<DT>(x, rbase + j)));
+        uint32_t m = 0;
+        for (int seg = wir; seg < geo.nseg; seg += WPR) {
+          const SegChunks<DT> t = seg_load<DT, FULL>(x, geo, row_ok, cbase, seg, lane);
+          m = max(m, max(amax8_bits<DT>(t.c0), amax8_bits<DT>(t.c1)));
         }
-        amax = group_max_rt(amax, geo.lpr);
+        amax = amax_from_bits<DT>(m);
       }
-      const float g = row_ok ? nv_row_scale(mode, amax, given, given_stride, row, tensor_amax) : 1.0f;
-      const double rg = 1.0 / (double)g;
-      if (row_ok && sub == 0) row_scale[row] = g;
-      for (int it = 0; it < geo.niter; ++it) {
-        const int64_t j = sub + (int64_t)it * geo.lpr;
-        if (row_ok && j < geo.bpr) {
-          uint32_t w0, w1, sb;
-          nv_quant_block<DT>(ld16<DT>(x, rbase + j), g, rg, w0, w1, sb);
-          __builtin_nontemporal_store(w0, &packed[rbase + j].x);
-          __builtin_nontemporal_store(w1, &packed[rbase + j].y);
-          scales[rbase + j] = (uint8_t)sb;
-        }
+    }
+    if (mode == 0) {
+      amax = group_max<64>(amax);
+      if constexpr (WPR > 1) {
+        // One barrier per row group: a wave can rewrite part[buf] only after
+        // the next group's barrier, which every reader of it has passed.
+        if (lane == 0) part[buf][wave] = fbits(amax);
+        __syncthreads();
+        uint32_t m = 0;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) m = max(m, part[buf][(wave / WPR) * WPR + w]);
+        amax = bitsf(m);
+        buf ^= 1;
       }
+    }
+    float g = row_ok ? nv_row_scale(mode, amax, given, given_stride, row, tensor_amax) : 1.0f;
+    g = bitsf(__builtin_amdgcn_readfirstlane(fbits(g)));   // the same in every lane
+    const double rg = 1.0 / (double)g;
+    if (row_ok && wir == 0 && lane == 0) row_scale[row] = g;
+    if (nv_g_normal(g)) {
+      if constexpr (NIT > 0) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+          seg_quant<DT, FULL, true>(c[it], geo, row_ok, row, wir + it * WPR, lane, g, rg, packed, scales);
+      } else {
+        for (int seg = wir; seg < geo.nseg; seg += WPR)
+          seg_quant<DT, FULL, true>(seg_load<DT, FULL>(x, geo, row_ok, cbase, seg, lane), geo, row_ok,
+                                    row, seg, lane, g, rg, packed, scales);
+      }
+    } else {
+      if constexpr (NIT > 0) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+          seg_quant<DT, FULL, false>(c[it], geo, row_ok, row, wir + it * WPR, lane, g, rg, packed, scales);
+      } else {
+        for (int seg = wir; seg < geo.nseg; seg += WPR)
+          seg_quant<DT, FULL, false>(seg_load<DT, FULL>(x, geo, row_ok, cbase, seg, lane), geo, row_ok,
+                                     row, seg, lane, g, rg, packed, scales);
+      }
+    }
+  }
+}
+
+// Rows of fewer than 64 blocks: lane `sub` of the LPR lanes (a power of two
+// >= blocks per row) of a row owns block `sub` (16 elements, 32 bytes of
+// bfloat16), 64 / LPR rows per wave.
+template <int DT>
+__global__ __launch_bounds__(256) void k_nvfp4_quant_short(
+    const void* __restrict__ x, int64_t rows, int64_t bpr, int lpr, int mode,
+    const float* __restrict__ given, int64_t given_stride,
+    const uint32_t* __restrict__ tensor_amax, u32x2* __restrict__ packed,
+    uint8_t* __restrict__ scales, float* __restrict__ row_scale) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & (lpr - 1);
+  const int rows_per_wave = kWave / lpr;
+  const int rows_per_block = 4 * rows_per_wave;
+  const int row_in_block = (threadIdx.x >> 6) * rows_per_wave + lane / lpr;
+  const int64_t ngroups = (rows + rows_per_block - 1) / rows_per_block;
+  for (int64_t bg = blockIdx.x; bg < ngroups; bg += gridDim.x) {
+    const int64_t row = bg * rows_per_block + row_in_block;
+    const bool ok = row < rows && sub < bpr;
+    const int64_t blk = row * bpr + sub;
+    const Raw8<DT> lo = ok ? ld8<DT>(x, 2 * blk) : zero8<DT>();
+    const Raw8<DT> hi = ok ? ld8<DT>(x, 2 * blk + 1) : zero8<DT>();
+    const float ba = amax_from_bits<DT>(max(amax8_bits<DT>(lo), amax8_bits<DT>(hi)));
+    const float amax = (mode == 0) ? group_max_rt(ba, lpr) : 0.0f;
+    const bool row_ok = row < rows;
+    const float g = row_ok ? nv_row_scale(mode, amax, given, given_stride, row, tensor_amax) : 1.0f;
+    const double rg = 1.0 / (double)g;
+    if (row_ok && sub == 0) row_scale[row] = g;
+    if (ok) {
+      uint32_t sb;
+      const double rden = nv_block_recip(ba, g, rg, sb);
+      stream_st(u32x2{nv_codes8<DT>(lo, rden), nv_codes8<DT>(hi, rden)}, packed + blk);
+      scales[blk] = (uint8_t)sb;
     }
   }
 }
@@ -219,7 +354,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant(
       for (int u = 0; u < kDqUnroll; ++u) {
         const int64_t j = sub + (int64_t)(it0 + u) * geo.lpr;
         const bool ok = j < geo.cpr;
-        w[u] = ok ? __builtin_nontemporal_load(packed + rbase + j) : 0u;
+        w[u] = ok ? stream_ld(packed + rbase + j) : 0u;
         sb[u] = ok ? (uint32_t)scales[(rbase + j) >> 1] : 0u;
       }
 #pragma unroll
@@ -241,38 +376,52 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant(
   }
 }
 
-static NvRowGeom nv_geom(int64_t rows, int64_t K) {
-  NvRowGeom g;
-  g.rows = rows;
-  g.bpr = K / 16;
-  int lpr = 1;
-  while (lpr < 64 && lpr < g.bpr) lpr <<= 1;
-  g.lpr = lpr;
-  g.niter = (int)((g.bpr + lpr - 1) / lpr);
-  return g;
+// Segments a wave may hold in registers (1, 2, 4, or 8 when built so); rows
+// needing more than 4 waves x this many segments take the two-pass fallback.
+#ifndef MXQ_NV_MAX_NIT
+#define MXQ_NV_MAX_NIT 4
+#endif
+
+template <int DT, int WPR, bool FULL>
+static void launch_seg_f(int nit, dim3 grid, hipStream_t s, const void* x,
+                         const NvSegGeom& geo, int mode, const float* given,
+                         int64_t gs, const uint32_t* ta, uint32_t* p,
+                         uint8_t* sc, float* rs) {
+  const dim3 block(256);
+  switch (nit) {
+    case 1: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 1, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+    case 2: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 2, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+    case 4: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 4, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+#if MXQ_NV_MAX_NIT >= 8
+    case 8: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 8, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+#endif
+    default: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 0, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+  }
 }
 
-static int nv_grid(const NvRowGeom& g) {
-  const int64_t rows_per_wave = kWave / g.lpr;
-  const int64_t waves = (g.rows + rows_per_wave - 1) / rows_per_wave;
-  const int64_t max_blocks = 256 * 8;
-  int64_t b = (waves + 3) / 4;
-  return (int)(b < max_blocks ? (b > 0 ? b : 1) : max_blocks);
+template <int DT, int WPR>
+static void launch_seg_w(int nit, dim3 grid, hipStream_t s, const void* x,
+                         const NvSegGeom& geo, int mode, const float* given,
+                         int64_t gs, const uint32_t* ta, uint32_t* p,
+                         uint8_t* sc, float* rs) {
+  if (geo.bpr % 64 == 0) launch_seg_f<DT, WPR, true>(nit, grid, s, x, geo, mode, given, gs, ta, p, sc, rs);
+  else launch_seg_f<DT, WPR, false>(nit, grid, s, x, geo, mode, given, gs, ta, p, sc, rs);
 }
 
 template <int DT>
-static void launch_nvq(int nit, dim3 grid, hipStream_t s, const void* x,
-                       NvRowGeom geo, int mode, const float* given,
-                       int64_t gs, const uint32_t* ta, uint2* p,
+static void launch_seg(int nit, int wpr, dim3 grid, hipStream_t s, const void* x,
+                       const NvSegGeom& geo, int mode, const float* given,
+                       int64_t gs, const uint32_t* ta, uint32_t* p,
                        uint8_t* sc, float* rs) {
-  const dim3 block(256);
-  switch (nit) {
-    case 1: hipLaunchKernelGGL((k_nvfp4_quant<DT, 1>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
-    case 2: hipLaunchKernelGGL((k_nvfp4_quant<DT, 2>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
-    case 4: hipLaunchKernelGGL((k_nvfp4_quant<DT, 4>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
-    case 8: hipLaunchKernelGGL((k_nvfp4_quant<DT, 8>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
-    default: hipLaunchKernelGGL((k_nvfp4_quant<DT, 0>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+  switch (wpr) {
+    case 1: launch_seg_w<DT, 1>(nit, grid, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+    case 2: launch_seg_w<DT, 2>(nit, grid, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+    default: launch_seg_w<DT, 4>(nit, grid, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
   }
+}
+
+static dim3 grid_of(int64_t units) {
+  return dim3((unsigned)(units < kMaxGridBlocks ? (units > 0 ? units : 1) : kMaxGridBlocks));
 }
 
 hipError_t launch_nvfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
@@ -280,7 +429,6 @@ hipError_t launch_nvfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
                               int64_t given_stride, float* scratch,
                               uint8_t* packed, uint8_t* scales,
                               float* row_scale, hipStream_t s) {
-  const NvRowGeom geo = nv_geom(rows, K);
   uint32_t* ta = reinterpret_cast<uint32_t*>(scratch);
   if (mode == 2) {
     const int64_t nchunks = rows * (K / 8);
@@ -293,18 +441,40 @@ hipError_t launch_nvfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
       default: hipLaunchKernelGGL(k_tensor_amax<DT_F16>, dim3(gb), dim3(256), 0, s, x, nchunks, ta); break;
     }
   }
-  // registers per lane hold NIT blocks (16 elements each): up to 8 (rows of
-  // 8192 columns when LPR = 64); longer rows take the two-pass fallback.
+  const int64_t bpr = K / 16;
+  if (bpr < 64) {
+    int lpr = 1;
+    while (lpr < bpr) lpr <<= 1;
+    const int64_t rows_per_block = 4 * (kWave / lpr);
+    const dim3 grid = grid_of((rows + rows_per_block - 1) / rows_per_block);
+    u32x2* p = reinterpret_cast<u32x2*>(packed);
+    switch (dt) {
+      case DT_F32: hipLaunchKernelGGL(k_nvfp4_quant_short<DT_F32>, grid, dim3(256), 0, s, x, rows, bpr, lpr, mode, given, given_stride, ta, p, scales, row_scale); break;
+      case DT_BF16: hipLaunchKernelGGL(k_nvfp4_quant_short<DT_BF16>, grid, dim3(256), 0, s, x, rows, bpr, lpr, mode, given, given_stride, ta, p, scales, row_scale); break;
+      default: hipLaunchKernelGGL(k_nvfp4_quant_short<DT_F16>, grid, dim3(256), 0, s, x, rows, bpr, lpr, mode, given, given_stride, ta, p, scales, row_scale); break;
+    }
+    return hipGetLastError();
+  }
+  NvSegGeom geo;
+  geo.rows = rows;
+  geo.bpr = bpr;
+  geo.cpr = 2 * bpr;
+  geo.nseg = (int)((bpr + 63) / 64);
+  // waves per row: the fewest (1, 2, 4) that leave each wave at most
+  // MXQ_NV_MAX_NIT segments; NIT = that count rounded up to a power of two.
+  int wpr = 1;
+  while (wpr < 4 && geo.nseg > MXQ_NV_MAX_NIT * wpr) wpr <<= 1;
+  const int per_wave = (geo.nseg + wpr - 1) / wpr;
   int nit = 1;
-  while (nit < geo.niter) nit <<= 1;
-  const int nit_max = (dt == DT_F32) ? 4 : 8;
-  if (nit > nit_max) nit = 0;
-  const dim3 grid(nv_grid(geo));
-  uint2* p = reinterpret_cast<uint2*>(packed);
+  while (nit < per_wave) nit <<= 1;
+  if (nit > MXQ_NV_MAX_NIT) { nit = 0; wpr = 4; }         // two passes over the row
+  const int64_t rows_per_block = 4 / wpr;
+  const dim3 grid = grid_of((rows + rows_per_block - 1) / rows_per_block);
+  uint32_t* p = reinterpret_cast<uint32_t*>(packed);
   switch (dt) {
-    case DT_F32: launch_nvq<DT_F32>(nit, grid, s, x, geo, mode, given, given_stride, ta, p, scales, row_scale); break;
-    case DT_BF16: launch_nvq<DT_BF16>(nit, grid, s, x, geo, mode, given, given_stride, ta, p, scales, row_scale); break;
-    default: launch_nvq<DT_F16>(nit, grid, s, x, geo, mode, given, given_stride, ta, p, scales, row_scale); break;
+    case DT_F32: launch_seg<DT_F32>(nit, wpr, grid, s, x, geo, mode, given, given_stride, ta, p, scales, row_scale); break;
+    case DT_BF16: launch_seg<DT_BF16>(nit, wpr, grid, s, x, geo, mode, given, given_stride, ta, p, scales, row_scale); break;
+    default: launch_seg<DT_F16>(nit, wpr, grid, s, x, geo, mode, given, given_stride, ta, p, scales, row_scale); break;
   }
   return hipGetLastError();
 }
@@ -320,8 +490,7 @@ hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales,
   geo.lpr = lpr;
   geo.niter = (int)((geo.cpr + lpr - 1) / lpr);
   const int64_t waves = (rows + (kWave / lpr) - 1) / (kWave / lpr);
-  int64_t nb = (waves + 3) / 4;
-  const dim3 grid((unsigned)(nb < 2048 ? (nb > 0 ? nb : 1) : 2048)), block(256);
+  const dim3 grid = grid_of((waves + 3) / 4), block(256);
   const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
   switch (dt) {
     case DT_F32: hipLaunchKernelGGL(k_nvfp4_dequant<DT_F32>, grid, block, 0, s, p, scales, row_scale, geo, y); break;

@@ -106,15 +106,39 @@ MXQ_HD float e2m1_decode(uint32_t c) {
 
 // ---------------------------------------------------------------- e4m3
 
-// e4m3fn byte of u in [2^-9, 448]: round to nearest, ties to even.
+// e4m3fn byte of u in [2^-9, 448]: round to nearest, ties to even.  Both
+// ranges are evaluated and one is selected (no branches).  *value receives
+// the float32 value of the byte.
+MXQ_HD uint32_t e4m3_encode_pos_v(float u, float* value) {
+  // below 2^-6 the quantum is 2^-9: adding and removing 2^14 (ulp 2^-9)
+  // rounds to nearest even
+  const float r = (u + 16384.0f) - 16384.0f;
+  const uint32_t sub = (uint32_t)(r * 512.0f);                 // 1..8
+  // normal range: keep 3 mantissa bits, round to nearest even
+  const uint32_t b = fbits(u);
+  const uint32_t rb = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
+  const uint32_t nrm = (rb >> 20) - (120u << 3);                // rebias 127 -> 7
+  const bool small = u < 0.015625f;
+  *value = small ? r : bitsf(rb);
+  return small ? sub : nrm;
+}
+
 MXQ_HD uint32_t e4m3_encode_pos(float u) {
-  if (u < 0.015625f) {                       // below 2^-6: quantum 2^-9
-    float r = (u + 16384.0f) - 16384.0f;     // ulp(2^14) = 2^-9: RNE
-    return (uint32_t)(r * 512.0f);           // 1..8 (8 is 2^-6, byte 0x08)
-  }
-  uint32_t b = fbits(u);
-  b = b + 0x7FFFFu + ((b >> 20) & 1u);       // keep 3 mantissa bits, RNE
-  return (b >> 20) - (120u << 3);            // rebias exponent 127 -> 7
+  float v;
+  return e4m3_encode_pos_v(u, &v);
+}
+
+// e4m3fn byte and value of u in [2^-9, 448]: on the GPU the hardware fp8
+// converters, which round to nearest even and agree with e4m3_encode_pos_v
+// on every float32 of that range; on the host e4m3_encode_pos_v itself.
+MXQ_HD uint32_t e4m3_encode_clamped(float u, float* value) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t b = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, u, 0, false) & 0xFFu;
+  *value = __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+  return b;
+#else
+  return e4m3_encode_pos_v(u, value);
+#endif
 }
 
 // float32 value of a positive e4m3fn byte (0x00..0x7E).
@@ -262,9 +286,27 @@ MXQ_HD uint32_t nvfp4_block_scale(float a, float g, double rg, float* den) {
   float u = div6_rn(a);
   u = (float)((double)u * rg);
   u = fminf(fmaxf(u, 0.001953125f), 448.0f);
-  const uint32_t sb = e4m3_encode_pos(u);
-  *den = e4m3_decode_pos(sb) * g;
+  float sigma;
+  const uint32_t sb = e4m3_encode_clamped(u, &sigma);
+  *den = sigma * g;
   return sb;
+}
+
+// 1 / d in binary64 to within about 2^-52 relative error, for d a float32
+// value that is finite and non-zero.  On the GPU: the hardware reciprocal
+// refined by two Newton steps (the refinement the compiler's own binary64
+// division builds on; each step squares the relative error), on the host the
+// correctly rounded quotient.
+MXQ_HD double recip64(double d) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  double r = __builtin_amdgcn_rcp(d);
+  double e = fma(-d, r, 1.0);
+  r = fma(r, e, r);
+  e = fma(-d, r, 1.0);
+  return fma(r, e, r);
+#else
+  return 1.0 / d;
+#endif
 }
 
 // NVFP4: packed word of 8 codes for elements divided by den; `rden` is the
@@ -317,7 +359,7 @@ MXQ_HD CacheGroupScale cache_scale(int fmt, float a) {
     r.inv = bitsf((254u - (fbits(r.s) >> 23)) << 23);   // 2^-k, exact
   } else {
     const float u = fminf(fmaxf(a / 6.0f, 0.001953125f), 448.0f);
-    r.s = e4m3_decode_pos(e4m3_encode_pos(u));
+    e4m3_encode_clamped(u, &r.s);
     r.inv = 0.0f;                                      // nvfp4 divides by s
   }
   r.half_s = r.s * 0.5f;

@@ -12,6 +12,42 @@ namespace mxq {
 
 constexpr int kWave = 64;
 
+// Grid size of the streaming kernels: workgroups of 256 threads (4 waves).
+// The weight kernels launch one workgroup per unit of work, up to
+// kMaxGridBlocks, and loop only beyond that: with more workgroups than fit on
+// the chip at once the dispatcher hands out work as CUs free up, which
+// balances the XCDs and leaves no tail of workgroups that did not fit in the
+// first round (a grid of exactly the resident count is right only while the
+// register budget allows that many).  The cache kernels, with much smaller
+// tensors, use at most kCacheGridBlocks.
+#ifndef MXQ_BLOCKS_PER_CU
+#define MXQ_BLOCKS_PER_CU 1024
+#endif
+constexpr int64_t kMaxGridBlocks = 256 * MXQ_BLOCKS_PER_CU;
+#ifndef MXQ_CACHE_BLOCKS_PER_CU
+#define MXQ_CACHE_BLOCKS_PER_CU 8
+#endif
+constexpr int64_t kCacheGridBlocks = 256 * MXQ_CACHE_BLOCKS_PER_CU;
+
+// Streaming inputs and outputs are touched once: their global accesses carry
+// the non-temporal hint unless MXQ_TEMPORAL is defined.
+template <typename T>
+__device__ __forceinline__ T stream_ld(const T* p) {
+#ifdef MXQ_TEMPORAL
+  return *p;
+#else
+  return __builtin_nontemporal_load(p);
+#endif
+}
+template <typename T>
+__device__ __forceinline__ void stream_st(T v, T* p) {
+#ifdef MXQ_TEMPORAL
+  *p = v;
+#else
+  __builtin_nontemporal_store(v, p);
+#endif
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ chunks
@@ -29,16 +65,16 @@ __device__ __forceinline__ Raw8<DT> ld8(const void* base, int64_t chunk);
 
 template <>
 __device__ __forceinline__ Raw8<DT_BF16> ld8<DT_BF16>(const void* base, int64_t c) {
-  return Raw8<DT_BF16>{__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + c)};
+  return Raw8<DT_BF16>{stream_ld(reinterpret_cast<const u32x4*>(base) + c)};
 }
 template <>
 __device__ __forceinline__ Raw8<DT_F16> ld8<DT_F16>(const void* base, int64_t c) {
-  return Raw8<DT_F16>{__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + c)};
+  return Raw8<DT_F16>{stream_ld(reinterpret_cast<const u32x4*>(base) + c)};
 }
 template <>
 __device__ __forceinline__ Raw8<DT_F32> ld8<DT_F32>(const void* base, int64_t c) {
   const u32x4* p = reinterpret_cast<const u32x4*>(base) + 2 * c;
-  return Raw8<DT_F32>{__builtin_nontemporal_load(p), __builtin_nontemporal_load(p + 1)};
+  return Raw8<DT_F32>{stream_ld(p), stream_ld(p + 1)};
 }
 
 template <int DT>
@@ -89,12 +125,12 @@ __device__ __forceinline__ void st8(void* base, int64_t c, const float f[8]);
 template <>
 __device__ __forceinline__ void st8<DT_F32>(void* base, int64_t c, const float f[8]) {
   u32x4* p = reinterpret_cast<u32x4*>(base) + 2 * c;
-  __builtin_nontemporal_store(u32x4{fbits(f[0]), fbits(f[1]), fbits(f[2]), fbits(f[3])}, p);
-  __builtin_nontemporal_store(u32x4{fbits(f[4]), fbits(f[5]), fbits(f[6]), fbits(f[7])}, p + 1);
+  stream_st(u32x4{fbits(f[0]), fbits(f[1]), fbits(f[2]), fbits(f[3])}, p);
+  stream_st(u32x4{fbits(f[4]), fbits(f[5]), fbits(f[6]), fbits(f[7])}, p + 1);
 }
 template <>
 __device__ __forceinline__ void st8<DT_BF16>(void* base, int64_t c, const float f[8]) {
-  __builtin_nontemporal_store(u32x4{bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]),
+  stream_st(u32x4{bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]),
                                     bf16x2_rne(f[4], f[5]), bf16x2_rne(f[6], f[7])},
                               reinterpret_cast<u32x4*>(base) + c);
 }
@@ -104,7 +140,7 @@ __device__ __forceinline__ void st8<DT_F16>(void* base, int64_t c, const float f
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     w[i] = f32_to_f16_rne(f[2 * i]) | (f32_to_f16_rne(f[2 * i + 1]) << 16);
-  __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
+  stream_st(u32x4{w[0], w[1], w[2], w[3]},
                               reinterpret_cast<u32x4*>(base) + c);
 }
 

@@ -201,14 +201,15 @@ def test_mxfp4_fp32_planted_midpoints():
     assert_same(p, po, "packed")
 
 
+@pytest.mark.parametrize("RK", [(512, 256), (128, 1040)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_nvfp4_quotients_hugging_decision_boundaries(dtype):
+def test_nvfp4_quotients_hugging_decision_boundaries(dtype, RK):
     """Elements placed at m * den and at its neighbouring representable values
     for every e2m1 midpoint m, with arbitrary (given) row scales and power-of-two
     ones (exact ties)."""
-    say("nvfp4 boundary-hugging quotients", dtype)
+    say("nvfp4 boundary-hugging quotients", dtype, RK)
     rng = np.random.default_rng(17)
-    R, K = 512, 256
+    R, K = RK
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
     g = np.where(rng.random(R) < 0.5, np.exp2(rng.integers(-14, -4, R)), rng.random(R) * 1e-3 + 1e-6).astype(np.float32)
     x = np.zeros((R, K), np.float32)
@@ -261,7 +262,8 @@ def test_mxfp4_empty_inputs_launch_nothing():
 
 # ------------------------------------------------------------------ NVFP4
 
-NV_SHAPES = [(5, 16), (7, 48), (33, 512), (9, 2064), (6, 4096), (5, 7168), (3, 8208), (2, 3, 256)]
+NV_SHAPES = [(5, 16), (7, 48), (33, 512), (4, 1008), (3, 1040), (9, 2064), (6, 4096), (5, 7168),
+             (3, 8208), (2, 16400), (2, 3, 256)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
@@ -289,11 +291,12 @@ def test_nvfp4_sweep_specials():
                 oracle.dequantize_nvfp4(po, so, go, torch.bfloat16), "dequant")
 
 
-@pytest.mark.parametrize("kind", ["pow2", "random", "scalar", "edge"])
-def test_nvfp4_given_scales(kind):
-    say("nvfp4 given", kind)
+@pytest.mark.parametrize("K", [256, 2064])
+@pytest.mark.parametrize("kind", ["pow2", "random", "scalar", "edge", "negative", "bounds"])
+def test_nvfp4_given_scales(kind, K):
+    say("nvfp4 given", kind, K)
     rng = np.random.default_rng(3)
-    R, K = 96, 256
+    R = 96
     x = torch.from_numpy(rng.standard_normal((R, K)).astype(np.float32)).to(torch.bfloat16)
     if kind == "pow2":
         gv = torch.from_numpy(np.exp2(rng.integers(-12, -2, R)).astype(np.float32))
@@ -301,6 +304,14 @@ def test_nvfp4_given_scales(kind):
         gv = torch.from_numpy((rng.random(R) * 1e-3).astype(np.float32))
     elif kind == "scalar":
         gv = torch.tensor([3.7e-4])
+    elif kind == "negative":
+        gv = torch.from_numpy(-(rng.random(R) * 1e-3 + 1e-6).astype(np.float32))
+    elif kind == "bounds":
+        # both sides of 2^-100 and 2^100 (row scales in between need no
+        # zero / infinity handling of the block denominators)
+        b = np.array([2.0 ** -100, 2.0 ** 100], np.float32)
+        gv = torch.from_numpy(np.resize(np.concatenate(
+            [b, np.nextafter(b, np.float32(0)), np.nextafter(b, np.float32(np.inf)), b * 2, b / 2]), R))
     else:
         x[3] = 0
         gv = torch.from_numpy(np.resize(np.array([0.0, 1e-42, 1e30, np.inf, 2.0 ** -126, 3.0, 1e-20, 1e20],
@@ -308,6 +319,30 @@ def test_nvfp4_given_scales(kind):
     po, so, go = oracle.quantize_nvfp4(x, mode="given", given=gv)
     p, s, g = gpu_quantize_nvfp4(x.to(DEV), mode="given", given=gv)
     assert_same(g, go, "row scale"); assert_same(s, so, "scales"); assert_same(p, po, "packed")
+
+
+def test_nvfp4_block_scale_dense_amax():
+    """Block maxima a on a dense grid of float32 values (every 64th bit pattern
+    from just below 6 * 2^-9 to just above 2688) and around 6 * t for every
+    rounding tie t of e4m3, with row scale 1, so that the block scale byte is
+    e4m3(RN(a / 6)) across the whole range of the encoder; 1024-column rows."""
+    say("nvfp4 dense block amax")
+    lo = int(np.float32(6 * 2.0 ** -9 * 0.999).view(np.uint32))
+    hi = int(np.float32(2688 * 1.001).view(np.uint32))
+    grid = np.arange(lo, hi, 64, dtype=np.uint32)
+    e4 = torch.arange(1, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    ties = (e4[:-1] + e4[1:]) / 2
+    near = (np.float32(6.0) * ties.astype(np.float32)).view(np.uint32).astype(np.int64)
+    near = (near[:, None] + np.arange(-6, 7)[None, :]).reshape(-1).astype(np.uint32)
+    a = np.concatenate([grid, near]).view(np.float32)
+    a = np.resize(a, -(-a.size // 64) * 64)
+    c = np.linspace(1.0, -1.0, 16, dtype=np.float32)       # c[0] = 1: element 0 is the amax
+    x = torch.from_numpy((a[:, None] * c[None, :]).astype(np.float32).reshape(-1, 1024))
+    one = torch.ones(1)
+    po, so, go = oracle.quantize_nvfp4(x, mode="given", given=one)
+    p, s, g = gpu_quantize_nvfp4(x.to(DEV), mode="given", given=one)
+    assert_same(s, so, "scales")
+    assert_same(p, po, "packed")
 
 
 @pytest.mark.parametrize("shape", [(64, 128), (300, 4096), (17, 16)])
