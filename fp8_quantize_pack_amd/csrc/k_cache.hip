@@ -18,8 +18,9 @@
 // Generic path (anything else): one thread per group, scalar loads.
 //
 // The e2m1 formats round with the gfx950 scaled fp4 converter (round half
-// down; float32 inputs and nvfp4 quotients rounded up to 22 significant bits
-// first, which changes no decision) and decode with the exact fp4 dequantizer;
+// down through a one-ulp step toward zero and round-to-nearest-even; float32
+// inputs and nvfp4 quotients rounded up to 22 significant bits first, which
+// changes no decision) and decode with the exact fp4 dequantizer;
 // the nvfp4 quotient x / sigma is taken as a binary64 product with the
 // correctly rounded 1 / sigma: x has at most 24 significant bits and sigma 4,
 // so x / sigma is never a float32 decision boundary and lies at least 2^-29
@@ -37,64 +38,91 @@ struct CacheGeom {
   int niter;       // ceil(slots / lpr)
 };
 
+// Quantize-dequantize one 8-element chunk (index c, valid if ok) whose group
+// spans G neighbouring lanes.  Every lane of the wave calls this together
+// (the group amax is a DPP reduction); only valid chunks are stored.
+template <int DT, int FMT, int G>
+__device__ __forceinline__ void cache_chunk(const Raw8<DT>& raw, bool ok, void* __restrict__ y,
+                                            int64_t c) {
+  float f[8];
+  unpack8<DT>(raw, f);
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+  a = group_max<G>(a);
+  const CacheGroupScale gs = cache_scale(FMT, a);
+  float o[8];
+  if constexpr (FMT == FMT_FP8 || DT == DT_F16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = cache_qdq1(FMT, DT == DT_F32, f[i], gs);
+  } else {
+    // e2m1 formats: quantize with the scaled fp4 converter (round half
+    // down), decode exactly with the fp4 dequantizer.
+    float q[8];
+    float cvt_scale;
+    if constexpr (FMT == FMT_MXFP4) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = (DT == DT_F32) ? ceil22(f[i]) : f[i];
+      cvt_scale = gs.s;                         // power of two: x / s inside
+    } else {
+      const double rs = 1.0 / (double)gs.s;     // sigma: an e4m3 value
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f[i] * rs));
+      cvt_scale = 1.0f;
+    }
+    // A midpoint tie is a float32 subnormal only under an mxfp4 scale
+    // below 2^-124; waves holding one take the stochastic-rounding
+    // converts, which need no tie-down step.
+    const bool tiny = (FMT == FMT_MXFP4) && __any(gs.s < 0x1p-124f);
+    const uint32_t w = e2m1_canonical_zeros(__builtin_expect(tiny, 0) ? e2m1_pack8_hw(q, cvt_scale)
+                                                                       : e2m1_pack8_rne(q, cvt_scale));
+    if constexpr (FMT == FMT_MXFP4 && DT == DT_BF16) {
+      if (ok) stream_st(e2m1_unpack8_bf16_hw(w, gs.s), reinterpret_cast<u32x4*>(y) + c);
+      return;
+    } else if constexpr (FMT == FMT_MXFP4) {
+      e2m1_unpack8_f32_hw(w, gs.s, o);
+    } else {
+      e2m1_unpack8_f32_hw(w, 1.0f, o);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = o[i] * gs.s;  // exact
+    }
+  }
+  if (ok) st8<DT>(y, c, o);
+}
+
+// Row groups in flight per wave (their loads are issued together).
+#ifndef MXQ_CACHE_UNROLL
+#define MXQ_CACHE_UNROLL 2
+#endif
+constexpr int kCacheUnroll = MXQ_CACHE_UNROLL;
+
 template <int DT, int FMT, int B>
 __global__ __launch_bounds__(256) void k_cache_qdq(const void* __restrict__ x,
                                                    void* __restrict__ y,
                                                    CacheGeom geo) {
   constexpr int G = B / 8;   // lanes per group
+  constexpr int U = kCacheUnroll;
   const int lane = threadIdx.x & 63;
   const int sub = lane & (geo.lpr - 1);
   const int rows_per_wave = kWave / geo.lpr;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   const int64_t ngroups = (geo.rows + rows_per_wave - 1) / rows_per_wave;
-  for (int64_t wg = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-       wg < ngroups; wg += nwaves) {
-    const int64_t row = wg * rows_per_wave + lane / geo.lpr;
-    const bool row_ok = row < geo.rows;
-    const int64_t rbase = row * geo.cpr;
+  for (int64_t wg0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+       wg0 < ngroups; wg0 += nwaves * U) {
     for (int it = 0; it < geo.niter; ++it) {
       const int64_t j = sub + (int64_t)it * geo.lpr;
-      const bool ok = row_ok && j < geo.cpr;
-      float f[8];
-      unpack8<DT>(ok ? ld8<DT>(x, rbase + j) : zero8<DT>(), f);
-      float a = 0.0f;
+      Raw8<DT> r[U];
+      bool ok[U];
+      int64_t c[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-      a = group_max<G>(a);
-      const CacheGroupScale gs = cache_scale(FMT, a);
-      float o[8];
-      if constexpr (FMT == FMT_FP8 || DT == DT_F16) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = cache_qdq1(FMT, DT == DT_F32, f[i], gs);
-      } else {
-        // e2m1 formats: quantize with the scaled fp4 converter (round half
-        // down), decode exactly with the fp4 dequantizer.
-        float q[8];
-        float cvt_scale;
-        if constexpr (FMT == FMT_MXFP4) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) q[i] = (DT == DT_F32) ? ceil22(f[i]) : f[i];
-          cvt_scale = gs.s;                         // power of two: x / s inside
-        } else {
-          const double rs = 1.0 / (double)gs.s;     // sigma: an e4m3 value
-#pragma unroll
-          for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f[i] * rs));
-          cvt_scale = 1.0f;
-        }
-        const uint32_t w = e2m1_canonical_zeros(e2m1_pack8_hw(q, cvt_scale));
-        if constexpr (FMT == FMT_MXFP4 && DT == DT_BF16) {
-          if (ok) stream_st(e2m1_unpack8_bf16_hw(w, gs.s),
-                                              reinterpret_cast<u32x4*>(y) + rbase + j);
-          continue;
-        } else if constexpr (FMT == FMT_MXFP4) {
-          e2m1_unpack8_f32_hw(w, gs.s, o);
-        } else {
-          e2m1_unpack8_f32_hw(w, 1.0f, o);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = o[i] * gs.s;  // exact
-        }
+      for (int u = 0; u < U; ++u) {
+        const int64_t row = (wg0 + u * nwaves) * rows_per_wave + lane / geo.lpr;
+        ok[u] = row < geo.rows && j < geo.cpr;
+        c[u] = row * geo.cpr + j;
+        r[u] = ok[u] ? ld8<DT>(x, c[u]) : zero8<DT>();
       }
-      if (ok) st8<DT>(y, rbase + j, o);
+#pragma unroll
+      for (int u = 0; u < U; ++u) cache_chunk<DT, FMT, G>(r[u], ok[u], y, c[u]);
     }
   }
 }

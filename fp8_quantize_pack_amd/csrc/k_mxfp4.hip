@@ -8,15 +8,17 @@
 //
 // Layout of the work.  Blocks never straddle rows (K % 32 == 0), so the tensor
 // is a flat run of 8-element chunks.  A wavefront tile is kUnroll x 64 chunks:
-// in step u lane l owns chunk tile*512 + u*64 + l, so every vector load and
+// in step u lane l owns chunk tile*kUnroll*64 + u*64 + l, so every vector load and
 // store instruction of the wave touches one contiguous 1 KiB (bf16 input) or
 // 256 B (packed) range, and the 4 lanes of a quad own one 32-column block
-// (their amax is combined with two DPP quad permutes).  A tile covers 128
-// blocks, so its 128 scale bytes fill one 128-byte cache line.
+// (their amax is combined with two DPP quad permutes).  With kUnroll = 2 a
+// tile covers 32 blocks (1024 elements) and 32 contiguous scale bytes: small
+// tiles and many workgroups balance best across the chip.
 //
 // Rounding and packing use the gfx950 scaled fp4 converts (see
 // mxq_kernel_common.h): the quantizer divides by the block's power-of-two
-// scale and rounds half down; the dequantizer multiplies back exactly.
+// scale and, after a one-ulp step toward zero, rounds to nearest even --
+// together round half down; the dequantizer multiplies back exactly.
 // float32 inputs are first rounded up to 22 significant bits (ceil22), which
 // changes no e2m1 decision; bfloat16 and float16 values already fit.
 #include "mxq_kernel_common.h"
@@ -25,10 +27,10 @@
 namespace mxq {
 
 #ifndef MXQ_MX_UNROLL
-#define MXQ_MX_UNROLL 8
+#define MXQ_MX_UNROLL 2
 #endif
 constexpr int kUnroll = MXQ_MX_UNROLL;
-constexpr int kTileChunks = kUnroll * kWave;   // 512 chunks = 4096 elements
+constexpr int kTileChunks = kUnroll * kWave;   // chunks per wavefront tile
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_mxfp4_quant(
@@ -59,7 +61,12 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = ceil22(f[i]);
       }
-      const uint32_t word = e2m1_pack8_hw(f, e8m0_as_scale(sb));
+      // Scale bytes below 3 can put a midpoint tie on a float32 subnormal,
+      // which the tie-down multiply cannot move: such waves (amax < 2^-121)
+      // take the stochastic-rounding converts.
+      const uint32_t word = __builtin_expect(__any(sb < 3u), 0)
+                                ? e2m1_pack8_hw(f, e8m0_as_scale(sb))
+                                : e2m1_pack8_rne(f, e8m0_as_scale(sb));
       if (c < nchunks) {
         stream_st(word, packed + c);
         if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sb;

@@ -29,7 +29,8 @@
 // (1 / den correctly rounded), rounds it to float32 -- which lands on the same
 // side of every decision boundary as x / den (see nvfp4_quant8 in
 // mxq_device.h) -- rounds that up to 22 significant bits (ceil22, again
-// decision-preserving) and lets the scaled fp4 converter round half down.
+// decision-preserving) and lets the fp4 converter round half down
+// (e2m1_pack8_rne).
 #include "mxq_kernel_common.h"
 #include "mxq_launch.h"
 
@@ -116,7 +117,7 @@ __device__ __forceinline__ uint32_t nv_codes8(const Raw8<DT>& r, double rden) {
   unpack8<DT>(r, f);
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = ceil22((float)((double)f[i] * rden));
-  return e2m1_pack8_hw(f, 1.0f);
+  return e2m1_pack8_rne(f, 1.0f);      // quotients near a midpoint are normal
 }
 
 // Value of lane L ^ 1 (DPP quad_perm [1,0,3,2]; every lane has a source).
@@ -320,10 +321,11 @@ __global__ __launch_bounds__(256) void k_tensor_amax(const void* __restrict__ x,
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
-// Dequantization works on 8-element chunks (one packed dword, half a block)
-// so that every load and store instruction of a wavefront is contiguous:
-// lane `sub` of a row owns the chunks sub, sub + LPR, ..., kDqUnroll of them
-// in flight at a time.
+// Dequantization of short rows (fewer than kDqSegChunks chunks) works on
+// 8-element chunks (one packed dword, half a block) so that every load and
+// store instruction of a wavefront is contiguous: lane `sub` of a row owns the
+// chunks sub, sub + LPR, ..., kDqUnroll of them in flight at a time, 64 / LPR
+// rows per wave.
 struct NvChunkGeom {
   int64_t rows;
   int64_t cpr;      // 8-element chunks per row = K / 8
@@ -331,7 +333,10 @@ struct NvChunkGeom {
   int niter;        // ceil(cpr / lpr)
 };
 
-constexpr int kDqUnroll = 4;
+#ifndef MXQ_NVD_UNROLL
+#define MXQ_NVD_UNROLL 16
+#endif
+constexpr int kDqUnroll = MXQ_NVD_UNROLL;
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_nvfp4_dequant(
@@ -372,6 +377,54 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant(
         }
         st8<DT>(y, rbase + j, f);
       }
+    }
+  }
+}
+
+// Dequantization of rows of at least kDqSegChunks chunks: a wave owns one
+// segment of kDqSegChunks consecutive chunks of a row (lane l takes chunks
+// l, l + 64, ...), so every load and store instruction is contiguous, the
+// row and its scale are the same for the whole wave (scalar), and the grid
+// has many small units that the dispatcher spreads evenly.
+constexpr int kDqSegUnroll = 2;
+constexpr int kDqSegChunks = kDqSegUnroll * kWave;
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_nvfp4_dequant_seg(
+    const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+    const float* __restrict__ row_scale, int64_t rows, int64_t cpr, int64_t nseg,
+    void* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t units = rows * nseg;
+  for (int64_t unit = (int64_t)blockIdx.x * (blockDim.x >> 6) +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       unit < units; unit += nwaves) {
+    const int64_t row = unit / nseg;                     // uniform
+    const int64_t seg = unit - row * nseg;
+    const float g = row_scale[row];
+    const int64_t rbase = row * cpr;
+    uint32_t w[kDqSegUnroll], sb[kDqSegUnroll];
+#pragma unroll
+    for (int u = 0; u < kDqSegUnroll; ++u) {
+      const int64_t j = seg * kDqSegChunks + u * kWave + lane;
+      const bool ok = j < cpr;
+      w[u] = ok ? stream_ld(packed + rbase + j) : 0u;
+      sb[u] = ok ? (uint32_t)scales[(rbase + j) >> 1] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kDqSegUnroll; ++u) {
+      const int64_t j = seg * kDqSegChunks + u * kWave + lane;
+      float f[8];
+      if constexpr (DT == DT_F16) {
+        nvfp4_dequant8(w[u], sb[u], g, f);
+      } else {
+        const float sigma = e4m3_decode_any(sb[u]);
+        e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g;        // exact, then RN
+      }
+      if (j < cpr) st8<DT>(y, rbase + j, f);
     }
   }
 }
@@ -482,9 +535,21 @@ hipError_t launch_nvfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
 hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales,
                                 const float* row_scale, int64_t rows,
                                 int64_t K, void* y, int dt, hipStream_t s) {
+  const int64_t cpr = K / 8;
+  if (cpr >= kDqSegChunks) {
+    const int64_t nseg = (cpr + kDqSegChunks - 1) / kDqSegChunks;
+    const dim3 grid = grid_of((rows * nseg + 3) / 4), block(256);
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
+    switch (dt) {
+      case DT_F32: hipLaunchKernelGGL(k_nvfp4_dequant_seg<DT_F32>, grid, block, 0, s, p, scales, row_scale, rows, cpr, nseg, y); break;
+      case DT_BF16: hipLaunchKernelGGL(k_nvfp4_dequant_seg<DT_BF16>, grid, block, 0, s, p, scales, row_scale, rows, cpr, nseg, y); break;
+      default: hipLaunchKernelGGL(k_nvfp4_dequant_seg<DT_F16>, grid, block, 0, s, p, scales, row_scale, rows, cpr, nseg, y); break;
+    }
+    return hipGetLastError();
+  }
   NvChunkGeom geo;
   geo.rows = rows;
-  geo.cpr = K / 8;
+  geo.cpr = cpr;
   int lpr = 2;
   while (lpr < 64 && lpr < geo.cpr) lpr <<= 1;
   geo.lpr = lpr;

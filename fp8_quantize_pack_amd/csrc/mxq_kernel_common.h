@@ -199,6 +199,29 @@ __device__ __forceinline__ uint32_t e2m1_pack8_hw(const float f[8], float scale)
   return o ^ ((e ^ o) & 0x0F0F0F0Fu);          // low nibbles from e, high from o
 }
 
+// Round to nearest with ties to the smaller magnitude through the round-to-
+// nearest-even converter (one instruction per pair instead of two
+// stochastic-rounding ones, at a higher issue rate).  Each value is first
+// multiplied by kTieDown = 1 - 2^-24, which maps every normal float32 to its
+// neighbour one ulp closer to zero and keeps zeros: a value / scale exactly
+// on an e2m1 midpoint then lies just below it and rounds down, and one at
+// least 2 ulps above a midpoint (or anywhere below it) keeps its side.
+// Callers guarantee that spacing (values with at most 22 significant bits,
+// e.g. after ceil22, or widened bfloat16 / float16) and that values on a
+// midpoint are normal float32 numbers (for a power-of-two scale, scale >=
+// 2^-124).  The converter itself rounds every float32 exactly to nearest
+// even (checked on all |value / scale| < 8 for several scales).
+constexpr float kTieDown = 0x1.fffffep-1f;
+
+__device__ __forceinline__ uint32_t rne_fp4_pair(float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a * kTieDown, b * kTieDown, scale, 0);
+}
+
+__device__ __forceinline__ uint32_t e2m1_pack8_rne(const float f[8], float scale) {
+  return gather_byte0(rne_fp4_pair(f[0], f[1], scale), rne_fp4_pair(f[2], f[3], scale),
+                      rne_fp4_pair(f[4], f[5], scale), rne_fp4_pair(f[6], f[7], scale));
+}
+
 // Clear the sign bit of every zero-magnitude nibble (code 8 -> 0), so that it
 // decodes to +0.0 as the e2m1 table prescribes.
 __device__ __forceinline__ uint32_t e2m1_canonical_zeros(uint32_t w) {
