@@ -20,7 +20,6 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -31,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+CALIBRATION_BYTES = 36 * 2048 * 7168 * 2
 METRIC = "effective GB/s (in+out) for FP4 quant-pack & dequant; % of MI355X HBM peak"
 
 
@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--experts", type=int, default=256,
                     help="experts of the sweep (256 is the full workload)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a torch negation over one 36-expert chunk "
+                         "(reads and writes CALIBRATION_BYTES) for HBM counter calibration")
     return ap.parse_args()
 
 
@@ -55,15 +58,6 @@ def bytes_mx(n_elem: int) -> int:
 def bytes_nv(n_elem: int, rows: int) -> int:
     # bf16 in + packed + one e4m3 byte per 16 + one float32 per row
     return 2 * n_elem + n_elem // 2 + n_elem // 16 + 4 * rows
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "fp8_quantize_pack_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode()); h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, src_hash: str):
@@ -89,6 +83,7 @@ def main():
 
     import torch
     import fp8_quantize_pack_amd as mxq
+    from fp8_quantize_pack_amd.profiling import kernel_source_hash
     import synth
 
     dev = torch.device("cuda:0")
@@ -174,6 +169,8 @@ def main():
     fp4_ms = sum(ops[n]["ms"] for n in fp4)
     dom = max(ops, key=lambda n: ops[n]["ms"])
     src_hash = kernel_source_hash()
+    for o in ops.values():
+        o["bytes_per_launch"] = o["bytes"] // o["launches"]
     traffic = measured_traffic(dom, src_hash)
     achieved = ops[dom]["GBps"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
@@ -181,6 +178,14 @@ def main():
                 "traffic": traffic,
                 "algorithmic_bytes_per_launch": ops[dom]["bytes"] // ops[dom]["launches"],
                 "avg_launch_us": ops[dom]["avg_launch_us"]}
+
+    if args.calibrate_copy:
+        # a plain elementwise kernel of known traffic, outside the timed region
+        xs, ys = x[:synth.C5_CHUNK_EXPERTS], y[:synth.C5_CHUNK_EXPERTS]
+        assert xs.numel() * xs.element_size() == CALIBRATION_BYTES
+        for _ in range(3):
+            torch.neg(xs, out=ys)
+        torch.cuda.synchronize()
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
     cpu = None

@@ -31,6 +31,11 @@
  *     reported by the runtime returns MXQ_E_LAUNCH.
  *   - rows == 0 or K == 0 is valid and launches nothing.
  *   - Inputs are never written.  Outputs must not overlap inputs.
+ *   - Input elements must be finite.  The pages define nothing for NaN or
+ *     infinite elements; for them the codes and scales are unspecified (every
+ *     access stays in bounds and the call still returns MXQ_OK).  Degenerate
+ *     but finite cases are specified: all-zero blocks and rows, zero, tiny,
+ *     huge or infinite given NVFP4 row scales.
  *   - Thread-safe: no global state.
  *   - Packed nibble order: the even column in the low nibble, the following
  *     odd column in the high nibble ([mxfp4 page] and [nvfp4 page],

@@ -35,12 +35,22 @@
  *     written: g = A / 2688, u = (a / 6) / g, den = sigma * g, q = x / den;
  *  R6 NVFP4 block scales are clamped to [2^-9, 448] before the e4m3 cast
  *     (maxNum: a NaN ratio takes the lower bound);
+ *  R7 an NVFP4 "row" is one index of the flattened leading dims of a
+ *     contiguous [..., K] tensor (one row scale per row of the packed output);
+ *  R8 a given global scale is either one value per row or one value for all
+ *     rows;
  *  R9 cache scales: fp8 and mxfp4 use the power-of-two ceiling of
  *     amax / elem_max (elem_max 448 or 6), floored at the smallest normal
  *     binary32; nvfp4 uses a single e4m3 scale e4m3(clamp(amax / 6));
  *  R10 a partial last cache group behaves as if zero-padded;
  *  R11 the fp8 cache keeps the sign of zero; e2m1 codes decode through the
  *     table, whose index 8 holds +0.0;
+ *  R12 NaN and infinite input elements are outside the contract: the pages
+ *     define nothing for them, and what the formulas below give for them is
+ *     neither specified nor tested (NaN quotients that finite inputs produce,
+ *     such as 0 / 0 under a zero row scale, are covered by R1);
+ *  R13 float16 inputs and outputs use the same binary32 arithmetic, with one
+ *     final round-to-nearest-even into float16;
  *  R14 e4m3 encodes saturate at 448.
  */
 #include "mxq_oracle.h"

@@ -385,7 +385,7 @@ def test_nvfp4_dequant_every_code_every_scale(dtype):
 # ------------------------------------------------------------------ cache
 
 CACHE_CASES = [(512, 32), (128, 32), (512, 16), (120, 32), (100, 16), (96, 7), (64, 64),
-               (1024, 512), (40, 8), (24, 256)]
+               (1024, 512), (40, 8), (24, 256), (24, 1), (30, 3)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
