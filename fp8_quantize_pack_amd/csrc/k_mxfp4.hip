@@ -31,9 +31,13 @@ namespace mxq {
 #endif
 constexpr int kUnroll = MXQ_MX_UNROLL;
 constexpr int kTileChunks = kUnroll * kWave;   // chunks per wavefront tile
+#ifndef MXQ_MX_WAVES
+#define MXQ_MX_WAVES 4
+#endif
+constexpr int kMxWaves = MXQ_MX_WAVES;         // waves per workgroup
 
 template <int DT>
-__global__ __launch_bounds__(256) void k_mxfp4_quant(
+__global__ __launch_bounds__(64 * kMxWaves) void k_mxfp4_quant(
     const void* __restrict__ x, uint32_t* __restrict__ packed,
     uint8_t* __restrict__ scales, int64_t nchunks, int64_t ntiles) {
   const int lane = threadIdx.x & 63;
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(
 }
 
 template <int DT>
-__global__ __launch_bounds__(256) void k_mxfp4_dequant(
+__global__ __launch_bounds__(64 * kMxWaves) void k_mxfp4_dequant(
     const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
     void* __restrict__ y, int64_t nchunks, int64_t ntiles) {
   const int lane = threadIdx.x & 63;
@@ -122,9 +126,9 @@ __global__ __launch_bounds__(256) void k_mxfp4_dequant(
 }
 
 static int grid_for(int64_t ntiles) {
-  // One tile per wave, 4 waves per workgroup, up to the grid cap.
+  // One tile per wave, kMxWaves waves per workgroup, up to the grid cap.
   const int64_t max_blocks = kMaxGridBlocks;
-  int64_t b = (ntiles + 3) / 4;
+  int64_t b = (ntiles + kMxWaves - 1) / kMxWaves;
   return (int)(b < max_blocks ? (b > 0 ? b : 1) : max_blocks);
 }
 
@@ -132,7 +136,7 @@ hipError_t launch_mxfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
                               int8_t* packed, uint8_t* scales, hipStream_t s) {
   const int64_t nchunks = rows * (K / 8);
   const int64_t ntiles = (nchunks + kTileChunks - 1) / kTileChunks;
-  const dim3 grid(grid_for(ntiles)), block(256);
+  const dim3 grid(grid_for(ntiles)), block(64 * kMxWaves);
   uint32_t* p = reinterpret_cast<uint32_t*>(packed);
   switch (dt) {
     case DT_F32: hipLaunchKernelGGL(k_mxfp4_quant<DT_F32>, grid, block, 0, s, x, p, scales, nchunks, ntiles); break;
@@ -147,7 +151,7 @@ hipError_t launch_mxfp4_dequant(const int8_t* packed, const uint8_t* scales,
                                 hipStream_t s) {
   const int64_t nchunks = rows * (K / 8);
   const int64_t ntiles = (nchunks + kTileChunks - 1) / kTileChunks;
-  const dim3 grid(grid_for(ntiles)), block(256);
+  const dim3 grid(grid_for(ntiles)), block(64 * kMxWaves);
   const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
   switch (dt) {
     case DT_F32: hipLaunchKernelGGL(k_mxfp4_dequant<DT_F32>, grid, block, 0, s, p, scales, y, nchunks, ntiles); break;
