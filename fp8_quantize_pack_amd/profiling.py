@@ -45,11 +45,16 @@ BENCH_KERNELS = {
 CALIBRATION_MARK = "neg_kernel"
 
 
+# the sources of the kernels bench.py measures (names and contents hashed)
+CODEC_SOURCES = ("mxq_device.h", "mxq_kernel_common.h", "mxq_launch.h", "mxq_api.cpp",
+                 "k_mxfp4.hip", "k_nvfp4.hip", "k_cache.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of every file under csrc/ (names and contents)."""
+    """Hash of the codec kernel sources under csrc/."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in CODEC_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())

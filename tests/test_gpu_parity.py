@@ -201,13 +201,17 @@ def test_mxfp4_fp32_planted_midpoints():
     assert_same(p, po, "packed")
 
 
+@pytest.mark.parametrize("steps", ["near", "margin"])
 @pytest.mark.parametrize("RK", [(512, 256), (128, 1040)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_nvfp4_quotients_hugging_decision_boundaries(dtype, RK):
+def test_nvfp4_quotients_hugging_decision_boundaries(dtype, RK, steps):
     """Elements placed at m * den and at its neighbouring representable values
     for every e2m1 midpoint m, with arbitrary (given) row scales and power-of-two
-    ones (exact ties)."""
-    say("nvfp4 boundary-hugging quotients", dtype, RK)
+    ones (exact ties).  "near": within 2 units of the last place of the input
+    dtype; "margin" (float32): 6 to 20 units away."""
+    if steps == "margin" and dtype != torch.float32:
+        pytest.skip("bfloat16 neighbours are 2^16 float32 units apart")
+    say("nvfp4 boundary-hugging quotients", dtype, RK, steps)
     rng = np.random.default_rng(17)
     R, K = RK
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
@@ -221,7 +225,10 @@ def test_nvfp4_quotients_hugging_decision_boundaries(dtype, RK):
             blk[0] = np.float32(6.0 * den)            # block amax 6 * den: block scale = sigma
             m = mids[rng.integers(0, 7, 15)]
             t = (m * den).astype(np.float32)
-            step = rng.integers(-2, 3, 15)
+            if steps == "near":
+                step = rng.integers(-2, 3, 15)
+            else:
+                step = rng.integers(6, 21, 15) * np.where(rng.random(15) < 0.5, -1, 1)
             if dtype == torch.bfloat16:
                 tb = torch.from_numpy(t).to(torch.bfloat16).view(torch.int16).numpy().astype(np.int32)
                 tb = (tb + step).astype(np.int16)
