@@ -6,8 +6,9 @@ library (``fp8_quantize_pack_amd``) never imports it and shares no code with it.
 
 The arithmetic lives in ``mxq_oracle.c`` (plain scalar C, one element at a
 time, in the order the source pages state each step; see the header of that
-file for the citations and the readings of open points).  This module builds it
-with gcc and marshals torch CPU tensors to it; it does no arithmetic itself.
+file for the citations and the readings of open points), the grouped GEMM
+included.  This module builds it with gcc and marshals torch CPU tensors to it;
+it does no arithmetic itself.
 """
 from __future__ import annotations
 
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.orc_dequantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, vp, i32]
         L.orc_quantize_cache.restype = None
         L.orc_quantize_cache.argtypes = [vp, vp, i32, i64, i64, i32, i64]
+        L.orc_grouped_mm.restype = None
+        L.orc_grouped_mm.argtypes = [vp, i32, i64, vp, i32, i64, i64, i64, vp, i32,
+                                     vp, i64, vp, vp]
         _lib = L
     return _lib
 
@@ -202,6 +206,28 @@ def quantize_cache(x: torch.Tensor, fmt: str, block_size: int) -> torch.Tensor:
     lib().orc_quantize_cache(x.data_ptr(), y.data_ptr(), _DT[x.dtype], R, C,
                              _FMT[fmt], block_size)
     return y
+
+
+def grouped_mm(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor, trans: bool,
+               rows=None):
+    """Grouped GEMM of activations x [T, D_in] with dequantized expert weights
+    w [E, N, K] (in the activation dtype), rows grouped by the cumulative
+    counts offs [E]: forward (trans False) x @ W_e^T, backward (trans True)
+    x @ W_e.  Only the given rows (all by default) are computed.  Returns
+    (out, absout) in float64: the sums and the sums of |products|."""
+    x, w = _cpu(x).contiguous(), _cpu(w).contiguous()
+    offs = _cpu(offs.to(torch.int32)).contiguous()
+    T, din = x.shape
+    E, N, K = w.shape
+    assert din == (N if trans else K) and offs.numel() == E
+    rows = torch.arange(T, dtype=torch.int64) if rows is None else _cpu(torch.as_tensor(rows, dtype=torch.int64)).contiguous()
+    dout = K if trans else N
+    out = torch.empty(rows.numel(), dout, dtype=torch.float64)
+    absout = torch.empty_like(out)
+    lib().orc_grouped_mm(x.data_ptr(), _DT[x.dtype], T, w.data_ptr(), _DT[w.dtype], E, N, K,
+                         offs.data_ptr(), int(bool(trans)), rows.data_ptr(), rows.numel(),
+                         out.data_ptr(), absout.data_ptr())
+    return out, absout
 
 
 def store_values(v: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:

@@ -435,3 +435,43 @@ void orc_quantize_cache(const void* x, void* y, int dtype, int64_t rows,
       cache_group(x, y, dtype, r * C + c0, n, fmt);
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Grouped GEMM ([mxfp4 page] MXFP4GroupedMM.forward / backward, [nvfp4 page]
+ * NVFP4GroupedMM.forward / backward): the activations of expert e are rows
+ * offs[e-1] .. offs[e]-1 of x (offs[-1] = 0); the forward multiplies them by
+ * the transposed dequantized weights W_e^T ([N, K] stored, [K, N] used), the
+ * backward multiplies the output gradient by W_e.  The weights enter as the
+ * dequantized values in the activation dtype, as the pages' dequantize-then-
+ * grouped-matmul does.  Written as the plain sum of products, per output.
+ * ---------------------------------------------------------------------- */
+void orc_grouped_mm(const void* x, int xdt, int64_t T, const void* w, int wdt,
+                    int64_t E, int64_t N, int64_t K, const int32_t* offs,
+                    int trans, const int64_t* rows, int64_t nrows,
+                    double* out, double* absout) {
+  int64_t din = trans ? N : K, dout = trans ? K : N;
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t r = rows[i];
+    int64_t e = -1, lo = 0;
+    for (int64_t j = 0; j < E; ++j) {
+      int64_t hi = offs[j];
+      if (r >= lo && r < hi) { e = j; break; }
+      if (hi > lo) lo = hi;
+    }
+    for (int64_t o = 0; o < dout; ++o) {
+      double acc = 0.0, aacc = 0.0;
+      if (e >= 0 && r < T) {
+        for (int64_t d = 0; d < din; ++d) {
+          double xv = orc_load(x, xdt, r * din + d);
+          int64_t wi = trans ? (e * N + d) * K + o : (e * N + o) * K + d;
+          double wv = orc_load(w, wdt, wi);
+          acc += xv * wv;
+          aacc += fabs(xv * wv);
+        }
+      }
+      out[i * dout + o] = acc;
+      absout[i * dout + o] = aacc;
+    }
+  }
+}
+

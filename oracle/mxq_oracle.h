@@ -48,6 +48,18 @@ void orc_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales,
 void orc_quantize_cache(const void* x, void* y, int dtype, int64_t rows,
                         int64_t C, int fmt, int64_t block_size);
 
+/* Grouped GEMM over dequantized expert weights, selected output rows only.
+ * x [T, D_in] (dtype xdt), w [E, N, K] (dtype wdt: the dequantized weights in
+ * the activation dtype); rows of x are grouped by expert through the
+ * cumulative counts offs[E].  trans 0: D_in = K, out[i, n] = sum_k x[r, k] *
+ * w[e, n, k]; trans 1: D_in = N, out[i, k] = sum_n x[r, n] * w[e, n, k], for
+ * r = rows[i] and e its expert (a row in no group gives zeros).  Products and
+ * sums in binary64; absout receives sum |x * w| for each output. */
+void orc_grouped_mm(const void* x, int xdt, int64_t T, const void* w, int wdt,
+                    int64_t E, int64_t N, int64_t K, const int32_t* offs,
+                    int trans, const int64_t* rows, int64_t nrows,
+                    double* out, double* absout);
+
 #ifdef __cplusplus
 }
 #endif

@@ -600,3 +600,65 @@ def test_cache_fp8_keeps_negative_zero_fp4_formats_do_not():
     y4 = oracle.quantize_cache(x, "mxfp4", 32)
     assert torch.signbit(y8[0, 1].float()) and y8[0, 1].item() == 0
     assert not torch.signbit(y4[0, 1].float()) and y4[0, 1].item() == 0
+
+
+# ------------------------------------------------------------------ grouped GEMM
+# [mxfp4 page] MXFP4GroupedMM.forward / backward and [nvfp4 page]
+# NVFP4GroupedMM.forward / backward: expert e multiplies its contiguous token
+# rows by W_e^T (forward) or W_e (backward); offs holds cumulative counts.
+
+def _brute_grouped_mm(x, w, offs, trans):
+    """Pure-Python loops over exact Fractions of the float values."""
+    from fractions import Fraction
+    T, din = x.shape
+    E, N, K = w.shape
+    dout = K if trans else N
+    out = [[Fraction(0)] * dout for _ in range(T)]
+    lo = 0
+    for e in range(E):
+        hi = int(offs[e])
+        for r in range(lo, hi):
+            for o in range(dout):
+                acc = Fraction(0)
+                for d in range(din):
+                    wv = float(w[e, d, o]) if trans else float(w[e, o, d])
+                    acc += Fraction(float(x[r, d])) * Fraction(wv)
+                out[r][o] = acc
+        lo = max(lo, hi)
+    return out
+
+
+@pytest.mark.parametrize("trans", [False, True])
+def test_grouped_mm_bruteforce_tiny(trans):
+    g = torch.Generator().manual_seed(5)
+    E, N, K = 3, 5, 7
+    offs = torch.tensor([3, 3, 6], dtype=torch.int32)      # expert 1 has no tokens
+    T = 8                                                   # rows 6, 7 belong to no expert
+    x = torch.randn(T, N if trans else K, generator=g).to(torch.bfloat16)
+    w = torch.randn(E, N, K, generator=g).to(torch.bfloat16)
+    out, absout = oracle.grouped_mm(x, w, offs, trans)
+    ref = _brute_grouped_mm(x.float(), w.float(), offs, trans)
+    for r in range(T):
+        for o in range(out.shape[1]):
+            assert out[r, o].item() == float(ref[r][o]), (r, o)
+    assert torch.all(out[6:] == 0) and torch.all(absout[6:] == 0)
+    assert torch.all(absout >= out.abs())
+
+
+def test_grouped_mm_expert_isolation_and_scaling():
+    g = torch.Generator().manual_seed(6)
+    E, N, K, T = 4, 6, 10, 12
+    offs = torch.tensor([2, 5, 9, 12], dtype=torch.int32)
+    x = torch.randn(T, K, generator=g).to(torch.bfloat16)
+    w = torch.randn(E, N, K, generator=g).to(torch.bfloat16)
+    out, _ = oracle.grouped_mm(x, w, offs, False)
+    w2 = w.clone()
+    w2[2] = torch.randn(N, K, generator=g).to(torch.bfloat16)
+    out2, _ = oracle.grouped_mm(x, w2, offs, False)
+    assert torch.equal(out[:5], out2[:5]) and torch.equal(out[9:], out2[9:])
+    assert not torch.equal(out[5:9], out2[5:9])
+    out4, _ = oracle.grouped_mm((x.float() * 4).to(torch.bfloat16), w, offs, False)
+    assert torch.equal(out4, out * 4)                       # power-of-two scaling is exact
+    # the backward product with the transposed weights [E, K, N] is the forward one
+    outb, _ = oracle.grouped_mm(x, w.transpose(1, 2).contiguous(), offs, True)
+    assert torch.equal(outb, out)
