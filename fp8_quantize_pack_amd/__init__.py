@@ -53,8 +53,11 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mxq_quantize_nvfp4.argtypes = [vp, i32, i64, i64, i32, vp, i64, vp, vp, vp, vp, vp]
     L.mxq_dequantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, vp, i32, vp]
     L.mxq_quantize_cache.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp]
+    L.mxq_grouped_mm_mxfp4.argtypes = [vp, i32, i64, vp, vp, i64, i64, i64, vp, i32, vp, vp]
+    L.mxq_grouped_mm_nvfp4.argtypes = [vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, vp, vp]
     for f in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
-              "mxq_dequantize_nvfp4", "mxq_quantize_cache"):
+              "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_grouped_mm_mxfp4",
+              "mxq_grouped_mm_nvfp4"):
         getattr(L, f).restype = ctypes.c_int
     L.mxq_status_string.argtypes = [ctypes.c_int]
     L.mxq_status_string.restype = ctypes.c_char_p
@@ -155,6 +158,23 @@ def mxq_quantize_cache(x, y, fmt, block_size, stream=None) -> None:
     _check(lib.mxq_quantize_cache(_ptr(x), _ptr(y), _dt(x.dtype), _rows(x), C,
                                   FORMATS[fmt], int(block_size), _stream(x, stream)),
            "mxq_quantize_cache")
+
+
+def mxq_grouped_mm_mxfp4(x, packed, scales, offs, y, transpose=False, stream=None) -> None:
+    E, N, K = packed.shape[0], packed.shape[1], packed.shape[2] * 2
+    _check(lib.mxq_grouped_mm_mxfp4(_ptr(x), _dt(x.dtype), x.shape[0], _ptr(packed), _ptr(scales),
+                                    E, N, K, _ptr(offs), int(bool(transpose)), _ptr(y),
+                                    _stream(x, stream)),
+           "mxq_grouped_mm_mxfp4")
+
+
+def mxq_grouped_mm_nvfp4(x, packed, scales, row_scale, offs, y, transpose=False,
+                         stream=None) -> None:
+    E, N, K = packed.shape[0], packed.shape[1], packed.shape[2] * 2
+    _check(lib.mxq_grouped_mm_nvfp4(_ptr(x), _dt(x.dtype), x.shape[0], _ptr(packed), _ptr(scales),
+                                    _ptr(row_scale), E, N, K, _ptr(offs), int(bool(transpose)),
+                                    _ptr(y), _stream(x, stream)),
+           "mxq_grouped_mm_nvfp4")
 
 
 # ------------------------------------------------------------------ tensor API
@@ -262,6 +282,45 @@ def quantize_cache(values: torch.Tensor, format: str, block_size: int) -> torch.
         raise ValueError("tensors must live on a GPU")
     y = torch.empty_like(x)
     mxq_quantize_cache(x, y, format, block_size)
+    return y
+
+
+def _grouped_mm_out(x: torch.Tensor, packed: torch.Tensor, transpose: bool) -> torch.Tensor:
+    if x.dim() != 2 or packed.dim() != 3:
+        raise ValueError("x must be [tokens, in_dim] and packed [experts, out_dim, in_dim // 2]")
+    N, K = packed.shape[1], packed.shape[2] * 2
+    din, dout = (N, K) if transpose else (K, N)
+    if x.shape[1] != din:
+        raise ValueError(f"x has {x.shape[1]} columns, the weights need {din}")
+    return torch.empty(x.shape[0], dout, dtype=x.dtype, device=x.device)
+
+
+def grouped_mm_mxfp4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                     offs: torch.Tensor, transpose: bool = False) -> torch.Tensor:
+    """Grouped GEMM over MXFP4 expert weights ([mxfp4 page] MXFP4GroupedMM):
+    x [tokens, K] grouped by expert (offs: int32 cumulative counts), packed
+    [E, N, K // 2], scales [E, N, K // 32]; returns x @ W_e^T [tokens, N], or
+    with transpose=True x [tokens, N] @ W_e [tokens, K] (the backward product).
+    Rows outside every group are left uninitialised."""
+    x, packed, scales = _dev_input(x), _dev_input(packed), _dev_input(scales)
+    offs = _dev_input(offs.to(torch.int32))
+    y = _grouped_mm_out(x, packed, transpose)
+    mxq_grouped_mm_mxfp4(x, packed, scales.view(torch.uint8), offs, y, transpose)
+    return y
+
+
+def grouped_mm_nvfp4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                     row_scale: torch.Tensor, offs: torch.Tensor,
+                     transpose: bool = False) -> torch.Tensor:
+    """Grouped GEMM over NVFP4 expert weights ([nvfp4 page] NVFP4GroupedMM):
+    as grouped_mm_mxfp4, with e4m3 scales [E, N, K // 16] and float32
+    row_scale [E, N]."""
+    x, packed, scales = _dev_input(x), _dev_input(packed), _dev_input(scales)
+    row_scale = _dev_input(row_scale.to(torch.float32))
+    offs = _dev_input(offs.to(torch.int32))
+    y = _grouped_mm_out(x, packed, transpose)
+    mxq_grouped_mm_nvfp4(x, packed.view(torch.uint8), scales.view(torch.uint8), row_scale, offs,
+                         y, transpose)
     return y
 
 

@@ -20,7 +20,8 @@ LIB = os.path.join(HERE, "libmxq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["mxq_api.cpp", "k_mxfp4.hip", "k_nvfp4.hip", "k_cache.hip"]
+SOURCES = ["mxq_api.cpp", "k_mxfp4.hip", "k_nvfp4.hip", "k_cache.hip",
+           "mxq_api_gemm.cpp", "k_grouped_mm.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC",

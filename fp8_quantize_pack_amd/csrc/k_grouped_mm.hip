@@ -1,0 +1,281 @@
+// k_grouped_mm.hip -- grouped GEMM over packed fp4 expert weights with
+// dequantization on the fly, for gfx950 (bf16 MFMA).
+//
+// Method: "nemo_automodel.components.quantization.mxfp4", MXFP4GroupedMM
+// forward / backward, and "nemo_automodel.components.quantization.nvfp4",
+// NVFP4GroupedMM forward / backward.  Activations are grouped by expert:
+// expert e owns rows [offs[e-1], offs[e]) of x (offs[-1] = 0).  Its weights
+// W_e [N, K] are stored packed along K; they are dequantized into the
+// activation dtype exactly as dequantize_mxfp4 / dequantize_nvfp4 do, then
+//   forward  (TRANS = 0): y[t, n] = sum_k x[t, k] * W_e[n, k]   (x [T, K], y [T, N])
+//   backward (TRANS = 1): y[t, k] = sum_n x[t, n] * W_e[n, k]   (x [T, N], y [T, K])
+// with float32 accumulation and one rounding of each output to bfloat16.
+//
+// Work: a workgroup (4 waves, 2 x 2) computes a 128 x 128 output tile of one
+// expert with v_mfma_f32_32x32x16_bf16 (each wave 64 x 64 = 2 x 2 MFMA tiles),
+// stepping the reduction by 64.  Both operands are staged in LDS as
+// [row][reduction] bf16 with 16-byte row padding; the activation tile is
+// copied as is, the weight tile is dequantized in registers with the gfx950
+// fp4 converters on its way to LDS (transposed for the backward product).
+// The global loads of the next reduction step are issued before the MFMAs of
+// the current one.  Blocks map to (expert, token tile, output tile): the
+// per-expert tile counts come from offs through a workgroup prefix sum, so
+// the host never reads offs.
+#include "mxq_kernel_common.h"
+#include "mxq_launch_gemm.h"
+
+namespace mxq {
+
+namespace gmm {
+
+constexpr int BM = 128;         // token rows per tile
+constexpr int BN = 128;         // output columns per tile
+constexpr int BK = 64;          // reduction step
+constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (16-byte pad)
+constexpr int THREADS = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct Args {
+  const uint16_t* x;          // [T, R] bf16 activations
+  const uint8_t* packed;      // [E, N, K/2]
+  const uint8_t* scales;      // [E, N, K/32] e8m0 or [E, N, K/16] e4m3
+  const float* row_scale;     // [E, N] (NVFP4)
+  const int32_t* offs;        // [E] cumulative token counts
+  uint16_t* y;                // [T, C] bf16
+  int64_t T, E, N, K;
+};
+
+// Dequantized bf16 of 8 consecutive weights (one packed dword) in the
+// arithmetic of dequantize_mxfp4 / dequantize_nvfp4 with a bf16 output.
+template <int FMT>
+__device__ __forceinline__ u32x4 deq8(uint32_t w, uint32_t sb, float g) {
+  const uint32_t wc = e2m1_canonical_zeros(w);
+  if constexpr (FMT == FMT_MXFP4) {
+    u32x4 o = e2m1_unpack8_bf16_hw(wc, e8m0_as_scale(sb));   // exact
+    if (sb == 255u) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    return o;
+  } else {
+    const float sigma = e4m3_decode_any(sb);
+    float f[8];
+    e2m1_unpack8_f32_hw(wc, 1.0f, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g;   // exact, then RN
+    return u32x4{bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]),
+                 bf16x2_rne(f[4], f[5]), bf16x2_rne(f[6], f[7])};
+  }
+}
+
+// Scale byte of weight (row n of expert e, column k).
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_at(const Args& a, int64_t row, int64_t k) {
+  constexpr int B = (FMT == FMT_MXFP4) ? 32 : 16;
+  return a.scales[row * (a.K / B) + k / B];
+}
+
+// Registers holding one reduction step of both operands in flight.
+struct Stage {
+  u32x4 av[4];                // 4 x 8 activations
+  u32x4 wv;                   // 32 packed codes (forward: one row; backward: one row quarter)
+  uint32_t sb[2];             // scale bytes
+  float g;                    // NVFP4 row scale
+};
+
+template <int FMT, int TRANS>
+__device__ __forceinline__ void load_stage(const Args& a, Stage& st, int tid, int64_t e,
+                                           int64_t m0, int64_t m1, int64_t c0, int64_t r0,
+                                           int64_t R) {
+  // activations: 128 rows x 64 columns = 1024 chunks of 8, 4 per thread
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + THREADS * i;
+    const int64_t row = m0 + (c >> 3);
+    st.av[i] = row < m1 ? stream_ld(reinterpret_cast<const u32x4*>(a.x + row * R + r0 + (c & 7) * 8))
+                        : u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (TRANS == 0) {
+    // W_e rows c0 .. c0+127, columns r0 .. r0+63: thread -> (row tid/2, half tid%2)
+    const int64_t row = e * a.N + c0 + (tid >> 1);
+    const int64_t k = r0 + (tid & 1) * 32;
+    st.wv = stream_ld(reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2));
+    st.sb[0] = scale_at<FMT>(a, row, k);
+    st.sb[1] = (FMT == FMT_MXFP4) ? st.sb[0] : scale_at<FMT>(a, row, k + 16);
+    st.g = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
+  } else {
+    // W_e rows r0 .. r0+63 (reduction), columns c0 .. c0+127: thread -> (row
+    // tid/4, quarter tid%4 of 32 columns)
+    const int64_t row = e * a.N + r0 + (tid >> 2);
+    const int64_t k = c0 + (tid & 3) * 32;
+    st.wv = stream_ld(reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2));
+    st.sb[0] = scale_at<FMT>(a, row, k);
+    st.sb[1] = (FMT == FMT_MXFP4) ? st.sb[0] : scale_at<FMT>(a, row, k + 16);
+    st.g = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
+  }
+}
+
+template <int FMT, int TRANS>
+__device__ __forceinline__ void store_stage(const Stage& st, uint16_t* As, uint16_t* Bs, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + THREADS * i;
+    *reinterpret_cast<u32x4*>(As + (c >> 3) * LDS_STRIDE + (c & 7) * 8) = st.av[i];
+  }
+  const uint32_t w[4] = {st.wv.x, st.wv.y, st.wv.z, st.wv.w};
+  u32x4 d[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) d[j] = deq8<FMT>(w[j], st.sb[j >> 1], st.g);
+  if constexpr (TRANS == 0) {
+    uint16_t* dst = Bs + (tid >> 1) * LDS_STRIDE + (tid & 1) * 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + 8 * j) = d[j];
+  } else {
+    // transpose: weight (reduction row n, output column k) -> Bs[k][n]
+    const int n = tid >> 2, kq = (tid & 3) * 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        Bs[(kq + 8 * j + 2 * h) * LDS_STRIDE + n] = (uint16_t)(v[h] & 0xFFFFu);
+        Bs[(kq + 8 * j + 2 * h + 1) * LDS_STRIDE + n] = (uint16_t)(v[h] >> 16);
+      }
+    }
+  }
+}
+
+// Which expert and token tile this workgroup owns: tile counts per expert,
+// an inclusive prefix sum over the workgroup, and a search.  Returns false
+// when the slot is beyond the last tile.
+__device__ __forceinline__ bool find_tile(const Args& a, int64_t slot, int64_t& e_out,
+                                          int64_t& m0, int64_t& m1) {
+  __shared__ int64_t s_found[3];
+  __shared__ int64_t s_wave[THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_found[0] = -1;
+  __syncthreads();
+  int64_t base = 0;
+  for (int64_t e0 = 0; e0 < a.E; e0 += THREADS) {
+    const int64_t e = e0 + tid;
+    int64_t lo = 0, hi = 0, cnt = 0;
+    if (e < a.E) {
+      lo = e > 0 ? (int64_t)a.offs[e - 1] : 0;
+      hi = (int64_t)a.offs[e];
+      lo = lo < 0 ? 0 : (lo > a.T ? a.T : lo);
+      hi = hi < lo ? lo : (hi > a.T ? a.T : hi);
+      cnt = (hi - lo + BM - 1) / BM;
+    }
+    int64_t incl = cnt;            // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int64_t before = base;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    int64_t total = 0;
+    for (int w = 0; w < THREADS / 64; ++w) total += s_wave[w];
+    const int64_t first = before + incl - cnt;
+    if (cnt > 0 && slot >= first && slot < first + cnt) {
+      s_found[0] = e;
+      s_found[1] = lo + (slot - first) * BM;
+      s_found[2] = hi;
+    }
+    base += total;
+    __syncthreads();
+  }
+  e_out = s_found[0];
+  m0 = s_found[1];
+  m1 = s_found[2];
+  return e_out >= 0;
+}
+
+template <int FMT, int TRANS>
+__global__ __launch_bounds__(THREADS) void k_grouped_mm(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t R = TRANS ? a.N : a.K;      // reduction length
+  const int64_t C = TRANS ? a.K : a.N;      // output columns
+  int64_t e, m0, m1;
+  if (!find_tile(a, blockIdx.x, e, m0, m1)) return;   // uniform over the workgroup
+  const int64_t c0 = (int64_t)blockIdx.y * BN;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;   // wave tile origin
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  Stage st;
+  load_stage<FMT, TRANS>(a, st, tid, e, m0, m1, c0, 0, R);
+  for (int64_t r0 = 0; r0 < R; r0 += BK) {
+    store_stage<FMT, TRANS>(st, As, Bs, tid);
+    __syncthreads();
+    if (r0 + BK < R) load_stage<FMT, TRANS>(a, st, tid, e, m0, m1, c0, r0 + BK, R);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                    As + (wm + 32 * i + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                    Bs + (wn + 32 * j + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: accumulator register q of lane l is row 8*(q/4) + 4*(l/32) +
+  // q%4, column l%32 of its 32 x 32 tile; one rounding to bf16
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int64_t col = c0 + wn + 32 * j + (lane & 31);
+        if (row < m1) a.y[row * C + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][q]);
+      }
+}
+
+}  // namespace gmm
+
+hipError_t launch_grouped_mm(const void* x, int64_t T, const uint8_t* packed,
+                             const uint8_t* scales, const float* row_scale,
+                             int64_t E, int64_t N, int64_t K, const int32_t* offs,
+                             int fmt, int trans, void* y, hipStream_t s) {
+  gmm::Args a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.packed = packed;
+  a.scales = scales;
+  a.row_scale = row_scale;
+  a.offs = offs;
+  a.y = static_cast<uint16_t*>(y);
+  a.T = T; a.E = E; a.N = N; a.K = K;
+  const int64_t C = trans ? K : N;
+  // x: token-tile slots (at most ceil(T / BM) + E over all experts; slots
+  // past the last tile exit at once), y: output tiles
+  const dim3 grid((unsigned)((T + gmm::BM - 1) / gmm::BM + E), (unsigned)(C / gmm::BN)), block(gmm::THREADS);
+  if (fmt == FMT_MXFP4) {
+    if (trans) hipLaunchKernelGGL((gmm::k_grouped_mm<FMT_MXFP4, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gmm::k_grouped_mm<FMT_MXFP4, 0>), grid, block, 0, s, a);
+  } else {
+    if (trans) hipLaunchKernelGGL((gmm::k_grouped_mm<FMT_NVFP4, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gmm::k_grouped_mm<FMT_NVFP4, 0>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mxq

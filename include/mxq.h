@@ -177,6 +177,42 @@ mxq_status mxq_quantize_cache(const void* x, void* y, mxq_dtype dt,
                               int64_t rows, int64_t C, mxq_format fmt,
                               int32_t block_size, hipStream_t stream);
 
+/*
+ * Grouped GEMM over packed fp4 expert weights, dequantized on the fly
+ * ([mxfp4 page] MXFP4GroupedMM, [nvfp4 page] NVFP4GroupedMM, forward and
+ * backward).
+ *   x       [tokens, D_in] bfloat16 activations (MXQ_BF16 only, else
+ *           MXQ_E_DTYPE), rows grouped contiguously by expert.
+ *   offs    [experts] int32 device array of cumulative token counts: expert e
+ *           owns rows [offs[e-1], offs[e]) (offs[-1] = 0).  It must be
+ *           non-decreasing with offs[experts-1] <= tokens; each group is
+ *           clamped to [0, tokens], so malformed offs cannot make an access
+ *           out of bounds (the results are then unspecified).
+ *   weights W [experts, N, K] packed along K as the quantize calls write them:
+ *           MXFP4: packed int8 [E, N, K/2] + e8m0 scales [E, N, K/32];
+ *           NVFP4: packed uint8 [E, N, K/2] + e4m3 scales [E, N, K/16] + float32
+ *           row_scale [E, N].  Each weight is dequantized to bfloat16 exactly
+ *           as mxq_dequantize_mxfp4 / mxq_dequantize_nvfp4 with MXQ_BF16 do.
+ *   transpose 0 (forward):  D_in = K, y [tokens, N], y[t] = x[t] @ W_e^T;
+ *             1 (backward): D_in = N, y [tokens, K], y[t] = x[t] @ W_e
+ *           (else MXQ_E_MODE).
+ *   y       bfloat16; float32 accumulation, one rounding per output.  Rows
+ *           outside every expert's group are not written.
+ *   N and K must be positive multiples of 128 (MXQ_E_SHAPE otherwise); x,
+ *   packed and y 16-byte aligned.  tokens == 0 or experts == 0 launches
+ *   nothing.
+ */
+mxq_status mxq_grouped_mm_mxfp4(const void* x, mxq_dtype xdt, int64_t tokens,
+                                const int8_t* packed, const uint8_t* scales,
+                                int64_t experts, int64_t N, int64_t K,
+                                const int32_t* offs, int32_t transpose, void* y,
+                                hipStream_t stream);
+mxq_status mxq_grouped_mm_nvfp4(const void* x, mxq_dtype xdt, int64_t tokens,
+                                const uint8_t* packed, const uint8_t* scales,
+                                const float* row_scale, int64_t experts, int64_t N,
+                                int64_t K, const int32_t* offs, int32_t transpose,
+                                void* y, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* mxq_status_string(mxq_status s);
 

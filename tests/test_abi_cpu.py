@@ -16,11 +16,11 @@ def _declared_functions():
     return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", src)))
 
 
-def test_header_declares_the_five_operations():
+def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
-              "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_status_string",
-              "mxq_abi_version"):
+              "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_grouped_mm_mxfp4",
+              "mxq_grouped_mm_nvfp4", "mxq_status_string", "mxq_abi_version"):
         assert n in names
 
 
@@ -87,6 +87,22 @@ def test_quantize_cache_validation(L):
     assert f(None, FAKE, 1, 4, 64, 0, 32, None) == 1
     assert f(None, None, 1, 0, 64, 0, 32, None) == 0
     assert f(FAKE, FAKE, 1, -2, 64, 0, 32, None) == 2
+
+
+def test_grouped_mm_validation(L):
+    f, g = L.mxq_grouped_mm_mxfp4, L.mxq_grouped_mm_nvfp4
+    # x, dt, tokens, packed, scales, E, N, K, offs, transpose, y, stream
+    ok = dict(x=FAKE, dt=1, T=64, p=FAKE, s=FAKE, E=4, N=256, K=512, offs=FAKE, tr=0, y=FAKE)
+    call = lambda **k: f(*[dict(ok, **k)[n] for n in ("x", "dt", "T", "p", "s", "E", "N", "K",
+                                                          "offs", "tr", "y")], None)
+    assert call(N=200) == 2 and call(K=96) == 2 and call(T=-1) == 2   # N, K multiples of 128
+    assert call(dt=0) == 3 and call(dt=2) == 3                         # bfloat16 only
+    assert call(tr=2) == 8
+    assert call(offs=None) == 1 and call(y=None) == 1
+    assert call(x=FAKE + 2) == 9 and call(p=FAKE + 8) == 9
+    assert call(T=0, x=None, p=None, s=None, offs=None, y=None) == 0   # empty: no launch
+    assert call(E=0) == 0
+    assert g(FAKE, 1, 64, FAKE, FAKE, None, 4, 256, 512, FAKE, 0, FAKE, None) == 1  # row_scale
 
 
 def test_status_strings(L):

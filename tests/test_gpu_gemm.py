@@ -1,0 +1,157 @@
+"""GPU parity of the grouped GEMM over packed fp4 expert weights
+([mxfp4 page] MXFP4GroupedMM, [nvfp4 page] NVFP4GroupedMM: forward x @ W_e^T,
+backward x @ W_e) against the oracle's binary64 sums, through the C ABI.
+
+Tolerance, from the arithmetic: every product of two bfloat16 values is exact
+in float32; a float32 sum of R products in any order is within
+(R - 1) * 2^-24 * sum|x w| of the exact sum (the bound is doubled here for
+accumulators that do not round each addition to nearest); one final rounding
+to bfloat16 adds at most 2^-9 relative.  So |y - ref| <= 2^-8 |ref| +
+R * 2^-22 * sum|x w|.  The weights are quantized by the oracle (never by the
+GPU path) and dequantized by it to bfloat16, as the pages' dequantize-then-
+grouped-matmul does; rows outside every expert's group must stay untouched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def mxq():
+    import fp8_quantize_pack_amd as m
+    return m
+
+
+def say(*a):
+    print("[gemm]", *a, flush=True)
+
+
+def _offs(counts):
+    return torch.tensor(np.cumsum(counts), dtype=torch.int32)
+
+
+def _weights(fmt, E, N, K, seed):
+    w = synth.moe_mxfp4((E, N, K), seed=seed) if fmt == "mxfp4" else synth.moe_nvfp4((E, N, K), seed=seed)
+    if fmt == "mxfp4":
+        p, s = oracle.quantize_mxfp4(w)
+        wd = oracle.dequantize_mxfp4(p, s, torch.bfloat16)
+        return (p, s), wd
+    p, s, g = oracle.quantize_nvfp4(w)
+    wd = oracle.dequantize_nvfp4(p, s, g, torch.bfloat16)
+    return (p, s, g), wd
+
+
+def _run(fmt, q, x, offs, transpose, y):
+    m = mxq()
+    xd, od = x.to(DEV), offs.to(DEV)
+    if fmt == "mxfp4":
+        p, s = q
+        m.mxq_grouped_mm_mxfp4(xd, p.to(DEV).view(torch.int8), s.to(DEV), od, y, transpose)
+    else:
+        p, s, g = q
+        m.mxq_grouped_mm_nvfp4(xd, p.to(DEV), s.to(DEV), g.to(DEV), od, y, transpose)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def _check(y, ref, absref, R, what):
+    yd = y.double()
+    tol = ref.abs() * 2.0 ** -8 + absref * R * 2.0 ** -22
+    bad = (yd - ref).abs() > tol
+    assert not bad.any(), (f"{what}: {int(bad.sum())} outputs beyond the bound; worst "
+                           f"{float(((yd - ref).abs() - tol).max())}")
+    # the bound is not vacuous: most outputs are the correctly rounded sum
+    exact = (y == ref.to(torch.bfloat16)).double().mean().item()
+    assert exact > 0.9, f"{what}: only {exact:.3f} of the outputs are the rounded exact sum"
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_grouped_mm_small_ragged(fmt, transpose):
+    """Three experts with 100, 0 and 213 tokens, 11 trailing rows in no group."""
+    E, N, K = 3, 256, 384
+    counts = [100, 0, 213]
+    T = sum(counts) + 11
+    say(fmt, "transpose" if transpose else "forward", E, N, K, T)
+    q, wd = _weights(fmt, E, N, K, seed=31)
+    g = torch.Generator().manual_seed(32)
+    x = torch.randn(T, N if transpose else K, generator=g).to(torch.bfloat16)
+    offs = _offs(counts)
+    sentinel = torch.full((T, K if transpose else N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = _run(fmt, q, x, offs, transpose, sentinel)
+    ref, absref = oracle.grouped_mm(x, wd, offs, transpose)
+    T0 = sum(counts)
+    _check(y[:T0], ref[:T0], absref[:T0], N if transpose else K, fmt)
+    assert torch.isnan(y[T0:].float()).all(), "rows outside every group were written"
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_grouped_mm_tile_edges(fmt):
+    """Groups that start and end inside 128-row tiles, single-token experts,
+    and a leading empty expert."""
+    E, N, K = 6, 128, 256
+    counts = [0, 1, 127, 129, 1, 255]
+    T = sum(counts)
+    q, wd = _weights(fmt, E, N, K, seed=33)
+    x = torch.randn(T, K, generator=torch.Generator().manual_seed(34)).to(torch.bfloat16)
+    offs = _offs(counts)
+    y = _run(fmt, q, x, offs, False, torch.empty(T, N, dtype=torch.bfloat16, device=DEV))
+    ref, absref = oracle.grouped_mm(x, wd, offs, False)
+    _check(y, ref, absref, K, fmt)
+
+
+def test_grouped_mm_wrapper_shapes_and_errors():
+    m = mxq()
+    E, N, K = 2, 128, 128
+    q, wd = _weights("mxfp4", E, N, K, seed=35)
+    x = torch.randn(10, K).to(torch.bfloat16).to(DEV)
+    offs = _offs([4, 6]).to(DEV)
+    y = m.grouped_mm_mxfp4(x, q[0].to(DEV).view(torch.int8), q[1].to(DEV), offs)
+    assert y.shape == (10, N) and y.dtype == torch.bfloat16
+    with pytest.raises(ValueError):
+        m.grouped_mm_mxfp4(x[:, :64], q[0].to(DEV).view(torch.int8), q[1].to(DEV), offs)
+    with pytest.raises(TypeError):
+        m.grouped_mm_mxfp4(x.float(), q[0].to(DEV).view(torch.int8), q[1].to(DEV), offs)
+
+
+# ------------------------------------------------------------------ per-expert shapes of C2 / C3
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_grouped_mm_mxfp4_c2_expert_shape(transpose):
+    """MXFP4 experts of the MoE config [*, 4096, 2048] (8 of the 32), ragged
+    token groups, compared on sampled rows of every group."""
+    E, N, K = 8, 4096, 2048
+    counts = [700, 0, 1, 513, 1024, 300, 129, 2000]
+    T = sum(counts)
+    say("mxfp4 C2 experts", transpose, T)
+    q, wd = _weights("mxfp4", E, N, K, seed=2)
+    x = (torch.randn(T, N if transpose else K, generator=torch.Generator().manual_seed(36)) * 0.5).to(torch.bfloat16)
+    offs = _offs(counts)
+    y = _run("mxfp4", q, x, offs, transpose,
+             torch.empty(T, K if transpose else N, dtype=torch.bfloat16, device=DEV))
+    ends = offs.tolist()
+    rows = sorted({r for a, b in zip([0] + ends[:-1], ends) if b > a for r in (a, b - 1, (a + b) // 2)})
+    ref, absref = oracle.grouped_mm(x, wd, offs, transpose, rows=rows)
+    _check(y[rows], ref, absref, N if transpose else K, "mxfp4 C2")
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_grouped_mm_nvfp4_c3_expert_shape(transpose):
+    """NVFP4 experts of the fused gate/up config [*, 3072, 4096] (4 of the 64)."""
+    E, N, K = 4, 3072, 4096
+    counts = [1500, 37, 0, 900]
+    T = sum(counts)
+    say("nvfp4 C3 experts", transpose, T)
+    q, wd = _weights("nvfp4", E, N, K, seed=3)
+    x = (torch.randn(T, N if transpose else K, generator=torch.Generator().manual_seed(37)) * 0.5).to(torch.bfloat16)
+    offs = _offs(counts)
+    y = _run("nvfp4", q, x, offs, transpose,
+             torch.empty(T, K if transpose else N, dtype=torch.bfloat16, device=DEV))
+    ends = offs.tolist()
+    rows = sorted({r for a, b in zip([0] + ends[:-1], ends) if b > a for r in (a, b - 1, (a + b) // 2)})
+    ref, absref = oracle.grouped_mm(x, wd, offs, transpose, rows=rows)
+    _check(y[rows], ref, absref, N if transpose else K, "nvfp4 C3")
