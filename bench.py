@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--experts", type=int, default=256,
                     help="experts of the sweep (256 is the full workload)")
+    ap.add_argument("--no-gemm", action="store_true",
+                    help="skip the grouped-GEMM measurement (not part of `value`)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a torch negation over one 36-expert chunk "
                          "(reads and writes CALIBRATION_BYTES) for HBM counter calibration")
@@ -179,6 +181,8 @@ def main():
                 "algorithmic_bytes_per_launch": ops[dom]["bytes"] // ops[dom]["launches"],
                 "avg_launch_us": ops[dom]["avg_launch_us"]}
 
+    gemm = None if args.no_gemm else grouped_gemm(torch, mxq, dev, max(args.steps, 1))
+
     if args.calibrate_copy:
         # a plain elementwise kernel of known traffic, outside the timed region
         xs, ys = x[:synth.C5_CHUNK_EXPERTS], y[:synth.C5_CHUNK_EXPERTS]
@@ -205,10 +209,55 @@ def main():
         "fp4_sweep_GBps": round(fp4_bytes / (fp4_ms * 1e-3) / 1e9, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "grouped_gemm": gemm,
         "ops": ops,
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(out), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def grouped_gemm(torch, mxq, dev, reps):
+    """The consumer of the codec: grouped GEMMs over packed expert weights,
+    dequantized on the fly, forward (x @ W_e^T) and backward (x @ W_e), on the
+    per-expert shapes of the MXFP4 MoE config (32 x [4096, 2048], 512 tokens
+    per expert) and the NVFP4 gate/up config (64 x [3072, 4096], 256 tokens
+    per expert); synthetic random codes and scales.  Timed with HIP events
+    around `reps` launches each; not part of `value`."""
+    g = torch.Generator(device=dev).manual_seed(11)
+    out = {"peak_TFLOPs": PEAK_BF16_TFLOPS, "bound": "mfma", "dtype": "bf16"}
+    for fmt, E, N, K, per in (("mxfp4", 32, 4096, 2048, 512), ("nvfp4", 64, 3072, 4096, 256)):
+        T = E * per
+        offs = torch.arange(1, E + 1, device=dev, dtype=torch.int32) * per
+        packed = torch.randint(0, 256, (E, N, K // 2), device=dev, dtype=torch.uint8, generator=g)
+        if fmt == "mxfp4":
+            scales = torch.randint(118, 126, (E, N, K // 32), device=dev, dtype=torch.uint8, generator=g)
+        else:
+            scales = torch.randint(0x30, 0x60, (E, N, K // 16), device=dev, dtype=torch.uint8, generator=g)
+            rs = torch.full((E, N), 1e-2, device=dev)
+        for tr in (False, True):
+            x = torch.randn(T, N if tr else K, device=dev, generator=g).to(torch.bfloat16)
+            y = torch.empty(T, K if tr else N, device=dev, dtype=torch.bfloat16)
+            if fmt == "mxfp4":
+                fn = lambda: mxq.mxq_grouped_mm_mxfp4(x, packed.view(torch.int8), scales, offs, y, tr)
+            else:
+                fn = lambda: mxq.mxq_grouped_mm_nvfp4(x, packed, scales, rs, offs, y, tr)
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / reps * 1e-3
+            tf = 2.0 * T * N * K / t / 1e12
+            out[f"{fmt}_{'backward' if tr else 'forward'}"] = {
+                "experts": E, "N": N, "K": K, "tokens": T, "avg_launch_us": round(t * 1e6, 1),
+                "TFLOPs": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
 
 
 def cpu_baseline(x_gpu, budget_s: float):

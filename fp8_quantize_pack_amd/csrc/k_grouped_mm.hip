@@ -11,15 +11,17 @@
 //   backward (TRANS = 1): y[t, k] = sum_n x[t, n] * W_e[n, k]   (x [T, N], y [T, K])
 // with float32 accumulation and one rounding of each output to bfloat16.
 //
-// Work: a workgroup (4 waves, 2 x 2) computes a 128 x 128 output tile of one
-// expert with v_mfma_f32_32x32x16_bf16 (each wave 64 x 64 = 2 x 2 MFMA tiles),
-// stepping the reduction by 64.  Both operands are staged in LDS as
+// Work: a workgroup (4 waves, 2 x 2) computes a BM x 128 output tile of one
+// expert (BM = 128 token rows) with v_mfma_f32_32x32x16_bf16 (each wave
+// BM/2 x 64 = BM/64 x 2 MFMA tiles), stepping the reduction by 64.
+// Both operands are staged in LDS as
 // [row][reduction] bf16 with 16-byte row padding; the activation tile is
 // copied as is, the weight tile is dequantized in registers with the gfx950
 // fp4 converters on its way to LDS (transposed for the backward product).
 // The global loads of the next reduction step are issued before the MFMAs of
-// the current one.  Blocks map to (expert, token tile, output tile): the
-// per-expert tile counts come from offs through a workgroup prefix sum, so
+// the current one.  Workgroups map to (expert, token tile, output tile) in an
+// XCD-aware order (see xcd_logical); the per-expert tile counts come from offs
+// through a workgroup prefix sum, so
 // the host never reads offs.
 #include "mxq_kernel_common.h"
 #include "mxq_launch_gemm.h"
@@ -28,8 +30,7 @@ namespace mxq {
 
 namespace gmm {
 
-constexpr int BM = 128;         // token rows per tile
-constexpr int BN = 128;         // output columns per tile
+constexpr int BN = 128;         // output columns per tile (token rows per tile: BM, 128 or 256)
 constexpr int BK = 64;          // reduction step
 constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (16-byte pad)
 constexpr int THREADS = 256;
@@ -75,20 +76,21 @@ __device__ __forceinline__ uint32_t scale_at(const Args& a, int64_t row, int64_t
 }
 
 // Registers holding one reduction step of both operands in flight.
+template <int BM>
 struct Stage {
-  u32x4 av[4];                // 4 x 8 activations
-  u32x4 wv;                   // 32 packed codes (forward: one row; backward: one row quarter)
-  uint32_t sb[2];             // scale bytes
-  float g;                    // NVFP4 row scale
+  u32x4 av[BM / 32];          // BM / 32 x 8 activations
+  u32x4 wv;                   // 32 packed codes of one weight row
+  uint32_t sb[2];             // scale bytes of the two 16-column halves
+  float g[1];                 // NVFP4 row scale
 };
 
-template <int FMT, int TRANS>
-__device__ __forceinline__ void load_stage(const Args& a, Stage& st, int tid, int64_t e,
+template <int FMT, int TRANS, int BM>
+__device__ __forceinline__ void load_stage(const Args& a, Stage<BM>& st, int tid, int64_t e,
                                            int64_t m0, int64_t m1, int64_t c0, int64_t r0,
                                            int64_t R) {
-  // activations: 128 rows x 64 columns = 1024 chunks of 8, 4 per thread
+  // activations: BM rows x 64 columns = 8 * BM chunks of 8, BM / 32 per thread
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < BM / 32; ++i) {
     const int c = tid + THREADS * i;
     const int64_t row = m0 + (c >> 3);
     st.av[i] = row < m1 ? stream_ld(reinterpret_cast<const u32x4*>(a.x + row * R + r0 + (c & 7) * 8))
@@ -101,40 +103,39 @@ __device__ __forceinline__ void load_stage(const Args& a, Stage& st, int tid, in
     st.wv = stream_ld(reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2));
     st.sb[0] = scale_at<FMT>(a, row, k);
     st.sb[1] = (FMT == FMT_MXFP4) ? st.sb[0] : scale_at<FMT>(a, row, k + 16);
-    st.g = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
+    st.g[0] = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
   } else {
     // W_e rows r0 .. r0+63 (reduction), columns c0 .. c0+127: thread -> (row
-    // tid/4, quarter tid%4 of 32 columns)
+    // tid/4, quarter tid%4 of 32 columns); 4 lanes read each row's 64 bytes
     const int64_t row = e * a.N + r0 + (tid >> 2);
     const int64_t k = c0 + (tid & 3) * 32;
     st.wv = stream_ld(reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2));
     st.sb[0] = scale_at<FMT>(a, row, k);
     st.sb[1] = (FMT == FMT_MXFP4) ? st.sb[0] : scale_at<FMT>(a, row, k + 16);
-    st.g = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
+    st.g[0] = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
   }
 }
 
-template <int FMT, int TRANS>
-__device__ __forceinline__ void store_stage(const Stage& st, uint16_t* As, uint16_t* Bs, int tid) {
+template <int FMT, int TRANS, int BM>
+__device__ __forceinline__ void store_stage(const Stage<BM>& st, uint16_t* As, uint16_t* Bs, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < BM / 32; ++i) {
     const int c = tid + THREADS * i;
     *reinterpret_cast<u32x4*>(As + (c >> 3) * LDS_STRIDE + (c & 7) * 8) = st.av[i];
   }
   const uint32_t w[4] = {st.wv.x, st.wv.y, st.wv.z, st.wv.w};
-  u32x4 d[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) d[j] = deq8<FMT>(w[j], st.sb[j >> 1], st.g);
   if constexpr (TRANS == 0) {
     uint16_t* dst = Bs + (tid >> 1) * LDS_STRIDE + (tid & 1) * 32;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(dst + 8 * j) = d[j];
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(dst + 8 * j) = deq8<FMT>(w[j], st.sb[j >> 1], st.g[0]);
   } else {
     // transpose: weight (reduction row n, output column k) -> Bs[k][n]
     const int n = tid >> 2, kq = (tid & 3) * 32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t v[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+      const u32x4 d = deq8<FMT>(w[j], st.sb[j >> 1], st.g[0]);
+      const uint32_t v[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         Bs[(kq + 8 * j + 2 * h) * LDS_STRIDE + n] = (uint16_t)(v[h] & 0xFFFFu);
@@ -147,6 +148,7 @@ __device__ __forceinline__ void store_stage(const Stage& st, uint16_t* As, uint1
 // Which expert and token tile this workgroup owns: tile counts per expert,
 // an inclusive prefix sum over the workgroup, and a search.  Returns false
 // when the slot is beyond the last tile.
+template <int BM>
 __device__ __forceinline__ bool find_tile(const Args& a, int64_t slot, int64_t& e_out,
                                           int64_t& m0, int64_t& m1) {
   __shared__ int64_t s_found[3];
@@ -192,35 +194,50 @@ __device__ __forceinline__ bool find_tile(const Args& a, int64_t slot, int64_t& 
   return e_out >= 0;
 }
 
-template <int FMT, int TRANS>
-__global__ __launch_bounds__(THREADS) void k_grouped_mm(Args a) {
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Logical tile L = xcd-major renumbering of the workgroup id, so that one
+// XCD runs a contiguous range of logical tiles (a bijection for any count).
+__device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t G) {
+  constexpr int64_t X = 8;
+  const int64_t xcd = b % X, pos = b / X, q = G / X, r = G % X;
+  return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
+}
+
+template <int FMT, int TRANS, int BM>
+__global__ __launch_bounds__(THREADS) void k_grouped_mm(Args a, int64_t ntiles_c) {
+  constexpr int MT = BM / 64;               // 32 x 32 MFMA tiles per wave along the tokens
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t R = TRANS ? a.N : a.K;      // reduction length
   const int64_t C = TRANS ? a.K : a.N;      // output columns
   int64_t e, m0, m1;
-  if (!find_tile(a, blockIdx.x, e, m0, m1)) return;   // uniform over the workgroup
-  const int64_t c0 = (int64_t)blockIdx.y * BN;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;   // wave tile origin
+  // logical tile -> (token slot, output tile), output tiles fastest: the
+  // tiles that share an activation tile, and then those that share an
+  // expert's weights, run next to each other on one XCD
+  const int64_t L = xcd_logical(blockIdx.x, gridDim.x);
+  const int64_t slot = L / ntiles_c;
+  if (!find_tile<BM>(a, slot, e, m0, m1)) return;   // uniform over the workgroup
+  const int64_t c0 = (L - slot * ntiles_c) * BN;
+  const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * 64;   // wave tile origin
 
-  f32x16 acc[2][2];
+  f32x16 acc[MT][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  Stage st;
-  load_stage<FMT, TRANS>(a, st, tid, e, m0, m1, c0, 0, R);
+  Stage<BM> st;
+  load_stage<FMT, TRANS, BM>(a, st, tid, e, m0, m1, c0, 0, R);
   for (int64_t r0 = 0; r0 < R; r0 += BK) {
-    store_stage<FMT, TRANS>(st, As, Bs, tid);
+    store_stage<FMT, TRANS, BM>(st, As, Bs, tid);
     __syncthreads();
-    if (r0 + BK < R) load_stage<FMT, TRANS>(a, st, tid, e, m0, m1, c0, r0 + BK, R);
+    if (r0 + BK < R) load_stage<FMT, TRANS, BM>(a, st, tid, e, m0, m1, c0, r0 + BK, R);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[MT], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MT; ++i)
         af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                     As + (wm + 32 * i + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)));
 #pragma unroll
@@ -228,7 +245,7 @@ __global__ __launch_bounds__(THREADS) void k_grouped_mm(Args a) {
         bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                     Bs + (wn + 32 * j + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
@@ -239,7 +256,7 @@ __global__ __launch_bounds__(THREADS) void k_grouped_mm(Args a) {
   // epilogue: accumulator register q of lane l is row 8*(q/4) + 4*(l/32) +
   // q%4, column l%32 of its 32 x 32 tile; one rounding to bf16
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -265,16 +282,21 @@ hipError_t launch_grouped_mm(const void* x, int64_t T, const uint8_t* packed,
   a.y = static_cast<uint16_t*>(y);
   a.T = T; a.E = E; a.N = N; a.K = K;
   const int64_t C = trans ? K : N;
-  // x: token-tile slots (at most ceil(T / BM) + E over all experts; slots
-  // past the last tile exit at once), y: output tiles
-  const dim3 grid((unsigned)((T + gmm::BM - 1) / gmm::BM + E), (unsigned)(C / gmm::BN)), block(gmm::THREADS);
+  // token-tile slots: at most ceil(T / bm) + E over all experts (slots past
+  // the last tile exit at once), times the output tiles
+  // 128-row token tiles (256-row tiles need 280 registers per lane, one wave
+  // per SIMD, and measured slower)
+  constexpr int bm = 128;
+  const int64_t slots = (T + bm - 1) / bm + E;
+  const int64_t ntc = C / gmm::BN;
+  const dim3 grid((unsigned)(slots * ntc)), block(gmm::THREADS);
+#define MXQ_GMM_LAUNCH(F, TR) hipLaunchKernelGGL((gmm::k_grouped_mm<F, TR, bm>), grid, block, 0, s, a, ntc)
   if (fmt == FMT_MXFP4) {
-    if (trans) hipLaunchKernelGGL((gmm::k_grouped_mm<FMT_MXFP4, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gmm::k_grouped_mm<FMT_MXFP4, 0>), grid, block, 0, s, a);
+    if (trans) MXQ_GMM_LAUNCH(FMT_MXFP4, 1); else MXQ_GMM_LAUNCH(FMT_MXFP4, 0);
   } else {
-    if (trans) hipLaunchKernelGGL((gmm::k_grouped_mm<FMT_NVFP4, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gmm::k_grouped_mm<FMT_NVFP4, 0>), grid, block, 0, s, a);
+    if (trans) MXQ_GMM_LAUNCH(FMT_NVFP4, 1); else MXQ_GMM_LAUNCH(FMT_NVFP4, 0);
   }
+#undef MXQ_GMM_LAUNCH
   return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@ mxq_status check(const void* x, mxq_dtype xdt, int64_t T, const void* packed,
   if (mul_overflows(E, N) || mul_overflows(E * N, K) || mul_overflows(T, N > K ? N : K) ||
       T > INT32_MAX)
     return MXQ_E_SIZE;
+  // one workgroup per (token-tile slot, output tile) in a 1-D grid
+  if (((T + kTile - 1) / kTile + E) * ((transpose ? K : N) / kTile) > INT32_MAX) return MXQ_E_SIZE;
   if (T == 0 || E == 0) return MXQ_OK;
   if (!x || !packed || !scales || !offs || !y) return MXQ_E_NULL;
   if (misaligned(x) || misaligned(packed) || misaligned(y)) return MXQ_E_ALIGN;

@@ -41,6 +41,10 @@ BENCH_KERNELS = {
     "cache_fp8": "mxq::k_cache_qdq<1, 0, 32>",
     "cache_mxfp4": "mxq::k_cache_qdq<1, 1, 32>",
     "cache_nvfp4": "mxq::k_cache_qdq<1, 2, 16>",
+    "gemm_mxfp4_forward": "mxq::gmm::k_grouped_mm<1, 0>",
+    "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1>",
+    "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0>",
+    "gemm_nvfp4_backward": "mxq::gmm::k_grouped_mm<2, 1>",
 }
 CALIBRATION_MARK = "neg_kernel"
 
@@ -75,14 +79,14 @@ def summarize_trace(stats_csv: str, command: str) -> str:
         f"# command: {command}",
         f"# kernel_source_hash: {kernel_source_hash()}",
         "# durations in microseconds over all dispatches (the sweep's last chunk holds 4 experts, the others 36)",
-        f"{'op':15s} {'kernel':42s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}",
+        f"{'op':20s} {'kernel':42s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}",
     ]
     by_kernel = {short_name(r["Name"]): r for r in rows}
     for op, k in BENCH_KERNELS.items():
         r = by_kernel.get(k)
         if r is None:
             continue
-        out.append(f"{op:15s} {k:42s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+        out.append(f"{op:20s} {k:42s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
                    f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
     others = [short_name(r["Name"]) for r in rows if short_name(r["Name"]) not in BENCH_KERNELS.values()]
     if others:
