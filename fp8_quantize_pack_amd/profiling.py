@@ -41,10 +41,10 @@ BENCH_KERNELS = {
     "cache_fp8": "mxq::k_cache_qdq<1, 0, 32>",
     "cache_mxfp4": "mxq::k_cache_qdq<1, 1, 32>",
     "cache_nvfp4": "mxq::k_cache_qdq<1, 2, 16>",
-    "gemm_mxfp4_forward": "mxq::gmm::k_grouped_mm<1, 0>",
-    "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1>",
-    "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0>",
-    "gemm_nvfp4_backward": "mxq::gmm::k_grouped_mm<2, 1>",
+    "gemm_mxfp4_forward": "mxq::gmm::k_grouped_mm<1, 0, 128>",
+    "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1, 128>",
+    "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0, 128>",
+    "gemm_nvfp4_backward": "mxq::gmm::k_grouped_mm<2, 1, 128>",
 }
 CALIBRATION_MARK = "neg_kernel"
 

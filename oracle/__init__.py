@@ -75,6 +75,21 @@ def lib() -> ctypes.CDLL:
         L.orc_dequantize_nvfp4.argtypes = [vp, vp, vp, i64, i64, vp, i32]
         L.orc_quantize_cache.restype = None
         L.orc_quantize_cache.argtypes = [vp, vp, i32, i64, i64, i32, i64]
+        L.orc_quantize_mxfp8.restype = None
+        L.orc_quantize_mxfp8.argtypes = [vp, i32, i64, i64, vp, vp]
+        L.orc_dequantize_mxfp8.restype = None
+        L.orc_dequantize_mxfp8.argtypes = [vp, vp, i64, i64, vp, i32]
+        L.orc_static_block_scale.restype = ctypes.c_float
+        L.orc_static_block_scale.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.orc_fake_quantize_fp4_static.restype = None
+        L.orc_fake_quantize_fp4_static.argtypes = [vp, i32, i64, i64, i64, vp,
+                                                   ctypes.c_float, vp]
+        L.orc_dequantize_kv_pages.restype = None
+        L.orc_dequantize_kv_pages.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, i32]
+        L.orc_k_smooth_row.restype = None
+        L.orc_k_smooth_row.argtypes = [vp, i64, i32]
+        L.orc_quantize_kv_nvfp4.restype = None
+        L.orc_quantize_kv_nvfp4.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp]
         L.orc_grouped_mm.restype = None
         L.orc_grouped_mm.argtypes = [vp, i32, i64, vp, i32, i64, i64, i64, vp, i32,
                                      vp, i64, vp, vp]
@@ -206,6 +221,96 @@ def quantize_cache(x: torch.Tensor, fmt: str, block_size: int) -> torch.Tensor:
     lib().orc_quantize_cache(x.data_ptr(), y.data_ptr(), _DT[x.dtype], R, C,
                              _FMT[fmt], block_size)
     return y
+
+
+def quantize_mxfp8(x: torch.Tensor):
+    """[..., K] -> (uint8 e4m3 codes [..., K], uint8 e8m0 scale bytes [..., K//32])."""
+    x = _cpu(x)
+    K = x.shape[-1]
+    assert K % 32 == 0
+    R = _rows(x.shape, K)
+    codes = torch.empty(*x.shape[:-1], K, dtype=torch.uint8)
+    scales = torch.empty(*x.shape[:-1], K // 32, dtype=torch.uint8)
+    lib().orc_quantize_mxfp8(x.data_ptr(), _DT[x.dtype], R, K, codes.data_ptr(),
+                             scales.data_ptr())
+    return codes, scales
+
+
+def dequantize_mxfp8(codes: torch.Tensor, scales: torch.Tensor,
+                     dtype: torch.dtype) -> torch.Tensor:
+    codes, scales = _cpu(codes), _cpu(scales)
+    K = codes.shape[-1]
+    R = _rows(codes.shape, K)
+    y = torch.empty(*codes.shape[:-1], K, dtype=dtype)
+    lib().orc_dequantize_mxfp8(codes.data_ptr(), scales.data_ptr(), R, K,
+                               y.data_ptr(), _DT[dtype])
+    return y
+
+
+def static_block_scale(a: float, global_amax: float) -> float:
+    """Dequantization-side block scale of the static two-level FP4 rule."""
+    return lib().orc_static_block_scale(a, global_amax)
+
+
+def fake_quantize_fp4_static(x: torch.Tensor, block_amax: torch.Tensor,
+                             global_amax: float, block: int) -> torch.Tensor:
+    """Static two-level FP4 quantize/dequantize; same shape and dtype as x.
+    block_amax holds one float32 per `block` consecutive columns."""
+    x = _cpu(x)
+    K = x.shape[-1]
+    assert K % block == 0
+    R = _rows(x.shape, K)
+    a = _cpu(block_amax.to(torch.float32)).reshape(-1)
+    assert a.numel() == R * (K // block)
+    y = torch.empty_like(x)
+    lib().orc_fake_quantize_fp4_static(x.data_ptr(), _DT[x.dtype], R, K, block,
+                                       a.data_ptr(), float(global_amax), y.data_ptr())
+    return y
+
+
+def dequantize_kv_pages(values, scales, amax, block_tokens: int, heads: int,
+                        dtype: torch.dtype) -> torch.Tensor:
+    """Blocks of a paged NVFP4 KV cache (lists of per-block tensors: uint8
+    [block_tokens*heads, D//2], uint8 [block_tokens*heads, D//16], one float
+    amax each) -> [1, nblocks*block_tokens, heads, D]."""
+    nb = len(values)
+    values = [_cpu(v) for v in values]
+    scales = [_cpu(s) for s in scales]
+    D = values[0].shape[-1] * 2
+    vp = (ctypes.c_void_p * nb)(*[v.data_ptr() for v in values])
+    sp = (ctypes.c_void_p * nb)(*[s.data_ptr() for s in scales])
+    am = _cpu(torch.as_tensor([float(a) for a in amax], dtype=torch.float32))
+    y = torch.empty(1, nb * block_tokens, heads, D, dtype=dtype)
+    lib().orc_dequantize_kv_pages(ctypes.cast(vp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
+                                  am.data_ptr(), nb, block_tokens, heads, D,
+                                  y.data_ptr(), _DT[dtype])
+    return y
+
+
+def k_smooth(x: torch.Tensor) -> torch.Tensor:
+    """k - mean(k, -1) in x's dtype (pairwise binary32 mean, rounded)."""
+    x = _cpu(x)
+    D = x.shape[-1]
+    rows = x.to(torch.float32).reshape(-1, D).contiguous()
+    L = lib()
+    for r in range(rows.shape[0]):
+        L.orc_k_smooth_row(rows[r].data_ptr(), D, _DT[x.dtype])
+    return rows.reshape(x.shape).to(x.dtype)
+
+
+def quantize_kv_nvfp4(k: torch.Tensor, smooth: bool = True):
+    """k [S, H, D] (or [1, S, H, D]) -> (uint8 packed [..., D//2], uint8 e4m3
+    bytes [..., D//16], float32 row scales [..., S, H]), one NVFP4 global
+    scale per head."""
+    k = _cpu(k)
+    S, H, D = k.shape[-3:]
+    lead = k.shape[:-1]
+    packed = torch.empty(*lead, D // 2, dtype=torch.uint8)
+    scales = torch.empty(*lead, D // 16, dtype=torch.uint8)
+    row_scale = torch.empty(*lead, dtype=torch.float32)
+    lib().orc_quantize_kv_nvfp4(k.data_ptr(), _DT[k.dtype], S, H, D, int(bool(smooth)),
+                                packed.data_ptr(), scales.data_ptr(), row_scale.data_ptr())
+    return packed, scales, row_scale
 
 
 def grouped_mm(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor, trans: bool,

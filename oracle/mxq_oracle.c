@@ -22,7 +22,13 @@
  *                quantize_cache, _power_of_two_ceiling, _CacheQuantization.
  *  [modelopt]    Model-Optimizer tensor_quantizer.py: TensorQuantizer.forward
  *                (inputs upcast to float before quantizing; blocks padded with
- *                zeros), _FP8_E4M3_MIN_POSITIVE (scale clamp).
+ *                zeros), _FP8_E4M3_MIN_POSITIVE (scale clamp),
+ *                TensorQuantizer._real_quantize (the MX branch and its MXFP8
+ *                case), _clamp_scale, _amax_to_scale,
+ *                StaticBlockScaleQuantizer._block_scale_from_amax and
+ *                StaticBlockScaleQuantizer._fake_quantize.
+ *  [longlive]    LongLive utils/quant.py: dequantize_kv_cache, k_smooth,
+ *                quantize_kv.
  *
  * Readings where the pages are silent, ambiguous or cut off:
  *  R1 midpoint ties go to the smaller magnitude (a count of midpoints strictly
@@ -52,11 +58,51 @@
  *  R13 float16 inputs and outputs use the same binary32 arithmetic, with one
  *     final round-to-nearest-even into float16;
  *  R14 e4m3 encodes saturate at 448.
+ *  R15 MXFP8 ([modelopt] _real_quantize, MX branch with e4m3 elements and
+ *     block 32): the pages print the dispatch but not the MXFP8 arithmetic.
+ *     The block scale follows the one fp8 rule with a power-of-two scale that
+ *     the pages do print ([cache page] quantize_cache, fp8): s = pow2ceil(
+ *     max(amax / 448, 2^-126)), stored as the e8m0 byte 127 + log2(s); the
+ *     codes are e4m3(x / s) (R11, R14); decoding multiplies the e4m3 value by
+ *     2^(b - 127) in binary32 and rounds once to the output dtype;
+ *  R16 static two-level FP4 ([modelopt] _block_scale_from_amax with FP8 block
+ *     scales, then _fake_quantize): binary32 throughout, left to right,
+ *       P  = G / 6, replaced by 1e-8 when <= 1e-8     (per-tensor scale)
+ *       m  = c * P with c = binary32(2^-9 / 448)      (smallest block scale)
+ *       s  = a / 6, replaced by m when <= m           (block scale)
+ *       t  = 448 / P; b = e4m3(s * t); s' = e4m3value(b) / t
+ *       y  = RN_dtype(e2m1(x / s') * s')
+ *     The e4m3 fake-quant under the amax P (scaled_e4m3 is named, not
+ *     printed) is taken as multiply by 448 / P, cast, divide by 448 / P.  The
+ *     printed division / cast / multiply with one amax for both the pre and
+ *     the post scale is taken as the static branch's arithmetic (its callee
+ *     is named, not printed); the fp4 cast rounds as R1 and R2;
+ *  R17 static FP4 amax inputs: one float32 block amax per B consecutive
+ *     columns of a row ([rows, K / B]) and one float32 global amax, all
+ *     finite and >= 0 (the quantizer's own amax validation rejects others);
+ *  R18 paged KV cache ([longlive] dequantize_kv_cache): block b holds the
+ *     rows t * H + h (token t < block_tokens, head h) of D columns, in
+ *     NVFP4 with row-major e4m3 scale bytes [block_tokens * H, D / 16] (the
+ *     swizzled layout of the page's third-party tensor class is out of
+ *     scope) and one float32 amax; its global scale is amax / (6 * 448) in
+ *     binary32 (the e2m1 and e4m3 maxima of the default scale rule); rows
+ *     decode as R5's NVFP4 and land at token b * block_tokens + t;
+ *  R19 k_smooth ([longlive] k_smooth): the mean over the last dim is the
+ *     binary32 pairwise sum (halves summed recursively, D a power of two)
+ *     times 1 / D, rounded to the tensor dtype; k - mean is evaluated in
+ *     binary32 and rounded to the dtype (reduced-precision tensors compute
+ *     in binary32 and round the result);
+ *  R20 quantize_kv ([longlive] quantize_kv): each head's [S, D] slice, after
+ *     k_smooth when it holds keys, is quantized to NVFP4 with the amax of the
+ *     whole slice (the quantize_nvfp4_modelopt rule: one global scale per
+ *     head, written to each of the head's rows); the page's MSE scale rule
+ *     belongs to a third-party library and is out of scope.
  */
 #include "mxq_oracle.h"
 
 #include <float.h>
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------------
@@ -475,3 +521,184 @@ void orc_grouped_mm(const void* x, int xdt, int64_t T, const void* w, int wdt,
   }
 }
 
+
+/* ------------------------------------------------------------------------
+ * MXFP8 real quantization ([modelopt] _real_quantize, MX branch, e4m3
+ * elements; reading R15)
+ * ---------------------------------------------------------------------- */
+
+#define MXFP8_BLOCK 32 /* the branch asserts MXFP8's block size of 32 */
+
+void orc_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_t K,
+                        uint8_t* codes, uint8_t* scales) {
+  int64_t nblk = K / MXFP8_BLOCK;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nblk; ++b) {
+      int64_t base = r * K + b * MXFP8_BLOCK;
+      /* step 1: block amax */
+      float amax = 0.0f;
+      for (int j = 0; j < MXFP8_BLOCK; ++j) {
+        float v = fabsf(orc_load(x, dtype, base + j));
+        if (v > amax) amax = v;
+      }
+      /* step 2: power-of-two scale >= amax / 448, floored at 2^-126 */
+      float s = orc_pow2_ceil(fmaxf(amax / E4M3_MAX, FLT_MIN));
+      int ex;
+      (void)frexpf(s, &ex);             /* s = 2^(ex - 1) */
+      scales[r * nblk + b] = (uint8_t)(ex - 1 + 127);
+      /* step 3: e4m3 of x / s, sign kept */
+      for (int j = 0; j < MXFP8_BLOCK; ++j) {
+        float v = orc_load(x, dtype, base + j);
+        codes[base + j] = (uint8_t)orc_e4m3_encode(v / s);
+      }
+    }
+  }
+}
+
+void orc_dequantize_mxfp8(const uint8_t* codes, const uint8_t* scales,
+                          int64_t rows, int64_t K, void* y, int dtype) {
+  int64_t nblk = K / MXFP8_BLOCK;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t i = r * K + k;
+      float scale = (float)orc_e8m0_decode(scales[r * nblk + k / MXFP8_BLOCK]);
+      float v = (float)orc_e4m3_decode(codes[i]) * scale;
+      orc_store(y, dtype, i, v);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Static two-level FP4 fake quantization ([modelopt]
+ * StaticBlockScaleQuantizer._block_scale_from_amax, _fake_quantize,
+ * _amax_to_scale, _clamp_scale, _FP8_E4M3_MIN_POSITIVE; readings R16, R17)
+ * ---------------------------------------------------------------------- */
+
+/* _clamp_scale: values at or below the floor are replaced by the floor. */
+static float clamp_scale_floor(float v, float floor_value) {
+  return (v <= floor_value) ? floor_value : v;
+}
+
+/* The dequantization-side block scale s' of a block with amax a under the
+ * global amax G (reading R16). */
+float orc_static_block_scale(float a, float G) {
+  /* _amax_to_scale(global_amax, 6) with the default floor 1e-8 */
+  float P = clamp_scale_floor(G / E2M1_MAX, 1e-8f);
+  /* smallest encodable block scale in physical units: (2^-9 / 448) * P */
+  float c = (float)(0x1p-9 / 448.0);
+  float m = c * P;
+  /* _amax_to_scale(amax, 6, min_value = m) */
+  float s = clamp_scale_floor(a / E2M1_MAX, m);
+  /* e4m3 fake quantization of s with P mapped to 448 */
+  float t = E4M3_MAX / P;
+  uint32_t byte = orc_e4m3_encode(s * t);
+  return (float)orc_e4m3_decode(byte) / t;
+}
+
+void orc_fake_quantize_fp4_static(const void* x, int dtype, int64_t rows,
+                                  int64_t K, int64_t block,
+                                  const float* block_amax, float G, void* y) {
+  int64_t nblk = K / block;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nblk; ++b) {
+      float sp = orc_static_block_scale(block_amax[r * nblk + b], G);
+      for (int64_t j = 0; j < block; ++j) {
+        int64_t i = r * K + b * block + j;
+        float v = orc_load(x, dtype, i);
+        float q = v / sp;                          /* quant_input */
+        uint32_t c = e2m1_code(v, q);              /* fp4 cast */
+        float w = (float)orc_e2m1_decode(c);
+        orc_store(y, dtype, i, w * sp);            /* times the post scale */
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Paged NVFP4 KV cache and k_smooth ([longlive] dequantize_kv_cache,
+ * k_smooth, quantize_kv; readings R18 - R20)
+ * ---------------------------------------------------------------------- */
+
+/* Block b of the cache: values[b] (uint8 [block_tokens * H, D / 2]),
+ * scales[b] (e4m3 bytes [block_tokens * H, D / 16]), amax[b] (one float).
+ * Output y: [nblocks * block_tokens, H, D] in dtype. */
+void orc_dequantize_kv_pages(const uint8_t* const* values,
+                             const uint8_t* const* scales, const float* amax,
+                             int64_t nblocks, int64_t block_tokens, int64_t H,
+                             int64_t D, void* y, int dtype) {
+  int64_t rows = block_tokens * H;
+  for (int64_t b = 0; b < nblocks; ++b) {
+    float g = amax[b] / (E2M1_MAX * E4M3_MAX);
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t d = 0; d < D; ++d) {
+        uint8_t byte = values[b][(r * D + d) / 2];
+        uint32_t code = (d & 1) ? (byte >> 4) : (byte & 15u);
+        float sigma = (float)orc_e4m3_decode(scales[b][r * (D / NVFP4_BLOCK) + d / NVFP4_BLOCK]);
+        float t = (float)orc_e2m1_decode(code) * sigma;
+        /* token b * block_tokens + t_in, head h: row b * rows + r of y */
+        orc_store(y, dtype, (b * rows + r) * D + d, t * g);
+      }
+    }
+  }
+}
+
+/* Pairwise binary32 sum of n values (n a power of two). */
+static float pairwise_sum(const float* v, int64_t n) {
+  if (n == 1) return v[0];
+  return pairwise_sum(v, n / 2) + pairwise_sum(v + n / 2, n / 2);
+}
+
+/* k_smooth of one row of D values in dtype, in place in `row` (R19). */
+void orc_k_smooth_row(float* row, int64_t D, int dtype) {
+  float mean = pairwise_sum(row, D) * (1.0f / (float)D);  /* exact scaling */
+  float m = mean;
+  if (dtype != 0) {            /* round the mean to the tensor dtype */
+    uint16_t h;
+    orc_store(&h, dtype, 0, mean);
+    m = orc_load(&h, dtype, 0);
+  }
+  for (int64_t d = 0; d < D; ++d) {
+    float diff = row[d] - m;
+    uint16_t h;
+    if (dtype != 0) {
+      orc_store(&h, dtype, 0, diff);
+      diff = orc_load(&h, dtype, 0);
+    }
+    row[d] = diff;
+  }
+}
+
+/* quantize_kv for one tensor k [S, H, D] (R20): per head, optional k_smooth
+ * of every row, then NVFP4 with the head slice's amax.  Outputs in the
+ * layout of k: packed [S, H, D / 2], scales [S, H, D / 16], row_scale [S, H]
+ * (the head's global scale on each of its rows). */
+void orc_quantize_kv_nvfp4(const void* k, int dtype, int64_t S, int64_t H,
+                           int64_t D, int smooth, uint8_t* packed,
+                           uint8_t* scales, float* row_scale) {
+  float* slice = (float*)malloc(sizeof(float) * (size_t)(S * D));
+  uint8_t* p = (uint8_t*)malloc((size_t)(S * D / 2));
+  uint8_t* sc = (uint8_t*)malloc((size_t)(S * D / NVFP4_BLOCK));
+  float* g = (float*)malloc(sizeof(float) * (size_t)S);
+  for (int64_t h = 0; h < H; ++h) {
+    /* the head's slice k[:, h, :], smoothed row by row */
+    for (int64_t s = 0; s < S; ++s) {
+      for (int64_t d = 0; d < D; ++d)
+        slice[s * D + d] = orc_load(k, dtype, (s * H + h) * D + d);
+      if (smooth) orc_k_smooth_row(slice + s * D, D, dtype);
+    }
+    /* NVFP4 of the slice with its whole-slice amax (mode 2); the smoothed
+     * values are dtype values, so quantizing their float32 copies is the
+     * same as quantizing the dtype tensor */
+    orc_quantize_nvfp4(slice, 0, S, D, 2, NULL, 0, p, sc, g);
+    for (int64_t s = 0; s < S; ++s) {
+      memcpy(packed + (s * H + h) * (D / 2), p + s * (D / 2), (size_t)(D / 2));
+      memcpy(scales + (s * H + h) * (D / NVFP4_BLOCK), sc + s * (D / NVFP4_BLOCK),
+             (size_t)(D / NVFP4_BLOCK));
+      row_scale[s * H + h] = g[s];
+    }
+  }
+  free(slice);
+  free(p);
+  free(sc);
+  free(g);
+}

@@ -1,6 +1,7 @@
 /*
  * mxq_oracle.h -- plain, slow CPU oracle for block-scaled microscaling
- * quantization (MXFP4, NVFP4, block-scaled cache QDQ).
+ * quantization (MXFP4, NVFP4, MXFP8, static two-level FP4, block-scaled
+ * cache QDQ, paged NVFP4 KV cache) and the grouped GEMM over its weights.
  *
  * TEST INFRASTRUCTURE ONLY.  This header and mxq_oracle.c are used by the
  * test-suite, by the smoke check and by the CPU-baseline leg of the bench.
@@ -47,6 +48,33 @@ void orc_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales,
 /* fmt 0: fp8 (e4m3 values, power-of-two scale), 1: mxfp4, 2: nvfp4 */
 void orc_quantize_cache(const void* x, void* y, int dtype, int64_t rows,
                         int64_t C, int fmt, int64_t block_size);
+
+/* MXFP8: e4m3 codes [rows, K] and e8m0 scale bytes [rows, K / 32]. */
+void orc_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_t K,
+                        uint8_t* codes, uint8_t* scales);
+void orc_dequantize_mxfp8(const uint8_t* codes, const uint8_t* scales,
+                          int64_t rows, int64_t K, void* y, int dtype);
+
+/* Static two-level FP4 fake quantization: block_amax [rows, K / block],
+ * global amax G; y has x's shape and dtype.  orc_static_block_scale gives
+ * the dequantization-side block scale of one block. */
+float orc_static_block_scale(float a, float G);
+void orc_fake_quantize_fp4_static(const void* x, int dtype, int64_t rows,
+                                  int64_t K, int64_t block,
+                                  const float* block_amax, float G, void* y);
+
+/* Paged NVFP4 KV cache -> contiguous [nblocks * block_tokens, H, D]; the
+ * three arrays hold one host pointer / value per block. */
+void orc_dequantize_kv_pages(const uint8_t* const* values,
+                             const uint8_t* const* scales, const float* amax,
+                             int64_t nblocks, int64_t block_tokens, int64_t H,
+                             int64_t D, void* y, int dtype);
+/* k_smooth of one row of D values (dtype values held as float32), in place. */
+void orc_k_smooth_row(float* row, int64_t D, int dtype);
+/* Per-head NVFP4 of k [S, H, D] (smooth != 0: k_smooth first). */
+void orc_quantize_kv_nvfp4(const void* k, int dtype, int64_t S, int64_t H,
+                           int64_t D, int smooth, uint8_t* packed,
+                           uint8_t* scales, float* row_scale);
 
 /* Grouped GEMM over dequantized expert weights, selected output rows only.
  * x [T, D_in] (dtype xdt), w [E, N, K] (dtype wdt: the dequantized weights in
