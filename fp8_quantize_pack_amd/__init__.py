@@ -15,6 +15,11 @@ Two layers, named after the C ABI and after the source pages:
   allocate and return new tensors with the dtypes and shapes the pages give
   ("nemo_automodel.components.quantization.mxfp4" / ".nvfp4" and
   "nemo_automodel.components.models.deepseek_v41.quantization").
+* ``quantize_mxfp8``, ``dequantize_mxfp8``, ``fake_quantize_fp4_static``:
+  ModelOpt's MX real quantization with e4m3 elements and its static
+  two-level FP4 quantizer (Model-Optimizer "tensor_quantizer.py").
+* ``grouped_mm_mxfp4``, ``grouped_mm_nvfp4``: the grouped expert GEMM over
+  packed weights.
 """
 from __future__ import annotations
 
@@ -55,9 +60,13 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mxq_quantize_cache.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp]
     L.mxq_grouped_mm_mxfp4.argtypes = [vp, i32, i64, vp, vp, i64, i64, i64, vp, i32, vp, vp]
     L.mxq_grouped_mm_nvfp4.argtypes = [vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, vp, vp]
+    L.mxq_quantize_mxfp8.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    L.mxq_dequantize_mxfp8.argtypes = [vp, vp, i64, i64, vp, i32, vp]
+    L.mxq_fake_quantize_fp4_static.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp]
     for f in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
               "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_grouped_mm_mxfp4",
-              "mxq_grouped_mm_nvfp4"):
+              "mxq_grouped_mm_nvfp4", "mxq_quantize_mxfp8", "mxq_dequantize_mxfp8",
+              "mxq_fake_quantize_fp4_static"):
         getattr(L, f).restype = ctypes.c_int
     L.mxq_status_string.argtypes = [ctypes.c_int]
     L.mxq_status_string.restype = ctypes.c_char_p
@@ -175,6 +184,29 @@ def mxq_grouped_mm_nvfp4(x, packed, scales, row_scale, offs, y, transpose=False,
                                     _ptr(row_scale), E, N, K, _ptr(offs), int(bool(transpose)),
                                     _ptr(y), _stream(x, stream)),
            "mxq_grouped_mm_nvfp4")
+
+
+def mxq_quantize_mxfp8(x, codes, scales, stream=None) -> None:
+    K = x.shape[-1]
+    _check(lib.mxq_quantize_mxfp8(_ptr(x), _dt(x.dtype), _rows(x), K, _ptr(codes),
+                                  _ptr(scales), _stream(x, stream)),
+           "mxq_quantize_mxfp8")
+
+
+def mxq_dequantize_mxfp8(codes, scales, y, stream=None) -> None:
+    K = y.shape[-1]
+    _check(lib.mxq_dequantize_mxfp8(_ptr(codes), _ptr(scales), _rows(y), K, _ptr(y),
+                                    _dt(y.dtype), _stream(y, stream)),
+           "mxq_dequantize_mxfp8")
+
+
+def mxq_fake_quantize_fp4_static(x, block_amax, global_amax, y, block_size,
+                                 stream=None) -> None:
+    K = x.shape[-1]
+    _check(lib.mxq_fake_quantize_fp4_static(_ptr(x), _dt(x.dtype), _rows(x), K,
+                                            int(block_size), _ptr(block_amax),
+                                            _ptr(global_amax), _ptr(y), _stream(x, stream)),
+           "mxq_fake_quantize_fp4_static")
 
 
 # ------------------------------------------------------------------ tensor API
@@ -321,6 +353,58 @@ def grouped_mm_nvfp4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
     y = _grouped_mm_out(x, packed, transpose)
     mxq_grouped_mm_nvfp4(x, packed.view(torch.uint8), scales.view(torch.uint8), row_scale, offs,
                          y, transpose)
+    return y
+
+
+MXFP8_BLOCK_SIZE = 32
+
+
+def quantize_mxfp8(weight: torch.Tensor):
+    """[..., K] (K % 32 == 0) -> (float8_e4m3fn codes [..., K],
+    float8_e8m0fnu scales [..., K//32]): the MX branch of ModelOpt's real
+    quantization with e4m3 elements."""
+    K = weight.shape[-1]
+    if K % MXFP8_BLOCK_SIZE:
+        raise ValueError(f"last dim {K} is not divisible by {MXFP8_BLOCK_SIZE}")
+    x = _dev_input(weight)
+    codes = torch.empty(*x.shape[:-1], K, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(*x.shape[:-1], K // 32, dtype=torch.uint8, device=x.device)
+    mxq_quantize_mxfp8(x, codes, scales)
+    return codes.view(torch.float8_e4m3fn), scales.view(torch.float8_e8m0fnu)
+
+
+def dequantize_mxfp8(codes: torch.Tensor, scales: torch.Tensor,
+                     dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """(e4m3 [..., K], e8m0 [..., K//32]) -> [..., K] in dtype."""
+    c = _dev_input(codes.view(torch.uint8))
+    s = _dev_input(scales.view(torch.uint8))
+    K = c.shape[-1]
+    if K % MXFP8_BLOCK_SIZE or s.shape[-1] != K // MXFP8_BLOCK_SIZE:
+        raise ValueError("codes/scales shapes do not describe 32-column blocks")
+    y = torch.empty(*c.shape, dtype=dtype, device=c.device)
+    mxq_dequantize_mxfp8(c, s, y)
+    return y
+
+
+def fake_quantize_fp4_static(x: torch.Tensor, block_amax: torch.Tensor,
+                             global_amax: torch.Tensor, block_size: int = 16) -> torch.Tensor:
+    """Static two-level FP4 quantize/dequantize (ModelOpt's
+    StaticBlockScaleQuantizer with FP8 block scales): x [..., K], block_amax
+    with one float32 per ``block_size`` consecutive columns ([..., K //
+    block_size]), global_amax one float32 (a device tensor); returns a new
+    tensor with x's shape and dtype."""
+    K = x.shape[-1]
+    if block_size < 8 or block_size > 1024 or block_size & (block_size - 1):
+        raise ValueError("block_size must be a power of two in [8, 1024]")
+    if K % block_size:
+        raise ValueError(f"last dim {K} is not a whole number of {block_size}-column blocks")
+    xi = _dev_input(x)
+    a = _dev_input(block_amax.to(device=xi.device, dtype=torch.float32))
+    if a.numel() != xi.numel() // block_size:
+        raise ValueError("block_amax must hold one value per block")
+    g = global_amax.to(device=xi.device, dtype=torch.float32).reshape(1).contiguous()
+    y = torch.empty_like(xi)
+    mxq_fake_quantize_fp4_static(xi, a, g, y, block_size)
     return y
 
 

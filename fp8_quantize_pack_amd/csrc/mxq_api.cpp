@@ -32,7 +32,7 @@ const char* mxq_status_string(mxq_status s) {
     case MXQ_E_SHAPE: return "invalid shape: negative size or last dim not a whole number of blocks";
     case MXQ_E_DTYPE: return "unknown dtype";
     case MXQ_E_FORMAT: return "unknown cache format";
-    case MXQ_E_BLOCK: return "block_size must be >= 1";
+    case MXQ_E_BLOCK: return "block_size out of the range the call accepts";
     case MXQ_E_SIZE: return "rows * K overflows int64";
     case MXQ_E_LAUNCH: return "kernel launch failed";
     case MXQ_E_MODE: return "unknown NVFP4 scale mode";

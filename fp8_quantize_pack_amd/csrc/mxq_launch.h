@@ -23,5 +23,13 @@ hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales,
                                 int64_t K, void* y, int dt, hipStream_t s);
 hipError_t launch_cache_qdq(const void* x, void* y, int dt, int64_t rows,
                             int64_t C, int fmt, int block_size, hipStream_t s);
+hipError_t launch_mxfp8_quant(const void* x, int dt, int64_t rows, int64_t K,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_mxfp8_dequant(const uint8_t* codes, const uint8_t* scales,
+                                int64_t rows, int64_t K, void* y, int dt,
+                                hipStream_t s);
+hipError_t launch_fp4_static_qdq(const void* x, int dt, int64_t rows, int64_t K,
+                                 int block_size, const float* block_amax,
+                                 const float* global_amax, void* y, hipStream_t s);
 
 } // namespace mxq

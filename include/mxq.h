@@ -11,10 +11,16 @@
  *   - the quantize/dequantize round trip used for cache values (fp8 e4m3,
  *     mxfp4 or nvfp4 groups of any block size).
  *
+ * Further calls: MXFP8 quantize / dequantize, static two-level FP4 fake
+ * quantization with caller-given amax values, and the grouped GEMM over
+ * packed fp4 expert weights.
+ *
  * Sources, cited by page title and section:
  *   [mxfp4 page] "nemo_automodel.components.quantization.mxfp4"
  *   [nvfp4 page] "nemo_automodel.components.quantization.nvfp4"
  *   [cache page] "nemo_automodel.components.models.deepseek_v41.quantization"
+ *   [modelopt]   Model-Optimizer "tensor_quantizer.py" (TensorQuantizer,
+ *                StaticBlockScaleQuantizer)
  *
  * Conventions shared by every call
  *   - Every data pointer is a DEVICE pointer to contiguous row-major memory
@@ -91,7 +97,7 @@ typedef enum mxq_status {
   MXQ_E_SHAPE = 2,   /* negative size, or K not a whole number of blocks     */
   MXQ_E_DTYPE = 3,   /* unknown mxq_dtype                                    */
   MXQ_E_FORMAT = 4,  /* unknown mxq_format                                   */
-  MXQ_E_BLOCK = 5,   /* cache block_size < 1                                 */
+  MXQ_E_BLOCK = 5,   /* block_size outside what the call accepts             */
   MXQ_E_SIZE = 6,    /* rows * K overflows int64                             */
   MXQ_E_LAUNCH = 7,  /* the HIP runtime rejected a kernel launch             */
   MXQ_E_MODE = 8,    /* unknown mxq_nv_mode                                  */
@@ -176,6 +182,59 @@ mxq_status mxq_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales,
 mxq_status mxq_quantize_cache(const void* x, void* y, mxq_dtype dt,
                               int64_t rows, int64_t C, mxq_format fmt,
                               int32_t block_size, hipStream_t stream);
+
+/*
+ * MXFP8 quantize ([modelopt] TensorQuantizer._real_quantize, the MX branch
+ * with e4m3 elements, which requires block size 32).  The pages name the
+ * MXFP8 tensor class without its arithmetic; the block scale is the fp8
+ * power-of-two rule of [cache page] quantize_cache / _power_of_two_ceiling.
+ *   x       [rows, K] of xdt; K % 32 == 0, else MXQ_E_SHAPE.
+ *   codes   [rows, K] float8_e4m3fn bytes: e4m3(x / s), round to nearest
+ *           even, sign bit of x kept (also on zeros); |x / s| <= 448 always.
+ *   scales  [rows, K/32] float8_e8m0fnu bytes of s = pow2ceil(max(amax / 448,
+ *           2^-126)) per 32-column block (bytes 1 .. 247 for finite input).
+ *   x and codes 16-byte aligned (MXQ_E_ALIGN otherwise).
+ */
+mxq_status mxq_quantize_mxfp8(const void* x, mxq_dtype xdt, int64_t rows,
+                              int64_t K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
+
+/*
+ * MXFP8 dequantize (the inverse of mxq_quantize_mxfp8).
+ *   codes [rows, K] e4m3 bytes, scales [rows, K/32] e8m0 bytes (K % 32 == 0).
+ *   y     [rows, K] of ydt: e4m3(code) * 2^(scale - 127), exact in float32
+ *         (or infinite when it overflows), rounded once to ydt; code bytes
+ *         0x7F / 0xFF and scale byte 0xFF give NaN.
+ *   codes and y 16-byte aligned.
+ */
+mxq_status mxq_dequantize_mxfp8(const uint8_t* codes, const uint8_t* scales,
+                                int64_t rows, int64_t K, void* y,
+                                mxq_dtype ydt, hipStream_t stream);
+
+/*
+ * Static two-level FP4 fake quantization ([modelopt]
+ * StaticBlockScaleQuantizer._block_scale_from_amax with FP8 block scales,
+ * _amax_to_scale, _clamp_scale, _FP8_E4M3_MIN_POSITIVE, and _fake_quantize
+ * with one amax as both the pre and the post scale).
+ *   x            [rows, K] of dt; y receives the round trip, same shape and dtype.
+ *   block_size   B: a power of two in [8, 1024] (else MXQ_E_BLOCK); K % B == 0
+ *                (else MXQ_E_SHAPE).
+ *   block_amax   [rows, K/B] float32 device array: the calibrated amax of each
+ *                block of B consecutive columns (finite, >= 0).
+ *   global_amax  one float32 in device memory (finite, >= 0).
+ *   float32 arithmetic, in this order:
+ *     P = G / 6 (1e-8 when <= 1e-8);  m = float32(2^-9 / 448) * P;
+ *     s = a / 6 (m when <= m);  t = 448 / P;  s' = e4m3(s * t) / t
+ *       (e4m3 round to nearest even, saturating at 448);
+ *     y = RN_dt(e2m1(x / s') * s')  (e2m1 ties to the smaller magnitude;
+ *       code 8 decodes to +0.0).
+ *   x and y 16-byte aligned.
+ */
+mxq_status mxq_fake_quantize_fp4_static(const void* x, mxq_dtype dt, int64_t rows,
+                                        int64_t K, int32_t block_size,
+                                        const float* block_amax,
+                                        const float* global_amax, void* y,
+                                        hipStream_t stream);
 
 /*
  * Grouped GEMM over packed fp4 expert weights, dequantized on the fly

@@ -20,7 +20,8 @@ def test_header_declares_the_operations():
     names = _declared_functions()
     for n in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
               "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_grouped_mm_mxfp4",
-              "mxq_grouped_mm_nvfp4", "mxq_status_string", "mxq_abi_version"):
+              "mxq_grouped_mm_nvfp4", "mxq_quantize_mxfp8", "mxq_dequantize_mxfp8",
+              "mxq_fake_quantize_fp4_static", "mxq_status_string", "mxq_abi_version"):
         assert n in names
 
 
@@ -103,6 +104,35 @@ def test_grouped_mm_validation(L):
     assert call(T=0, x=None, p=None, s=None, offs=None, y=None) == 0   # empty: no launch
     assert call(E=0) == 0
     assert g(FAKE, 1, 64, FAKE, FAKE, None, 4, 256, 512, FAKE, 0, FAKE, None) == 1  # row_scale
+
+
+def test_mxfp8_validation(L):
+    q, d = L.mxq_quantize_mxfp8, L.mxq_dequantize_mxfp8
+    assert q(FAKE, 1, 4, 48, FAKE, FAKE, None) == 2           # K % 32
+    assert q(FAKE, 3, 4, 64, FAKE, FAKE, None) == 3
+    assert q(FAKE, 1, 1 << 40, 1 << 30, FAKE, FAKE, None) == 6
+    assert q(FAKE, 1, 4, 64, FAKE, None, None) == 1
+    assert q(FAKE, 1, 4, 64, FAKE + 8, FAKE, None) == 9       # codes alignment
+    assert q(None, 1, 0, 64, None, None, None) == 0
+    assert d(FAKE, FAKE, 4, 16, FAKE, 1, None) == 2
+    assert d(FAKE, FAKE, 4, 64, FAKE, 5, None) == 3
+    assert d(None, FAKE, 4, 64, FAKE, 1, None) == 1
+    assert d(FAKE, FAKE, 4, 64, FAKE + 2, 1, None) == 9
+    assert d(None, None, 3, 0, None, 1, None) == 0
+
+
+def test_fp4_static_validation(L):
+    f = L.mxq_fake_quantize_fp4_static
+    # x, dt, rows, K, block, block_amax, global_amax, y, stream
+    assert f(FAKE, 1, 4, 64, 12, FAKE, FAKE, FAKE, None) == 5     # not a power of two
+    assert f(FAKE, 1, 4, 64, 4, FAKE, FAKE, FAKE, None) == 5      # below 8
+    assert f(FAKE, 1, 4, 4096, 2048, FAKE, FAKE, FAKE, None) == 5 # above 1024
+    assert f(FAKE, 1, 4, 48, 32, FAKE, FAKE, FAKE, None) == 2     # K % block
+    assert f(FAKE, 2 + 5, 4, 64, 16, FAKE, FAKE, FAKE, None) == 3
+    assert f(FAKE, 1, 4, 64, 16, FAKE, None, FAKE, None) == 1
+    assert f(FAKE, 1, 4, 64, 16, None, FAKE, FAKE, None) == 1
+    assert f(FAKE + 4, 1, 4, 64, 16, FAKE, FAKE, FAKE, None) == 9
+    assert f(None, 1, 0, 64, 16, None, None, None, None) == 0
 
 
 def test_status_strings(L):
