@@ -18,6 +18,9 @@ Two layers, named after the C ABI and after the source pages:
 * ``quantize_mxfp8``, ``dequantize_mxfp8``, ``fake_quantize_fp4_static``:
   ModelOpt's MX real quantization with e4m3 elements and its static
   two-level FP4 quantizer (Model-Optimizer "tensor_quantizer.py").
+* ``dequantize_kv_cache``, ``quantize_kv_nvfp4``: the NVFP4 KV cache of
+  LongLive's utils/quant.py (paged dequantization; per-head quantization
+  with k_smooth).
 * ``grouped_mm_mxfp4``, ``grouped_mm_nvfp4``: the grouped expert GEMM over
   packed weights.
 """
@@ -63,10 +66,13 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mxq_quantize_mxfp8.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     L.mxq_dequantize_mxfp8.argtypes = [vp, vp, i64, i64, vp, i32, vp]
     L.mxq_fake_quantize_fp4_static.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp]
+    L.mxq_dequantize_kv_pages_nvfp4.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
+    L.mxq_quantize_kv_nvfp4.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp, vp, vp]
     for f in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
               "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_grouped_mm_mxfp4",
               "mxq_grouped_mm_nvfp4", "mxq_quantize_mxfp8", "mxq_dequantize_mxfp8",
-              "mxq_fake_quantize_fp4_static"):
+              "mxq_fake_quantize_fp4_static", "mxq_dequantize_kv_pages_nvfp4",
+              "mxq_quantize_kv_nvfp4"):
         getattr(L, f).restype = ctypes.c_int
     L.mxq_status_string.argtypes = [ctypes.c_int]
     L.mxq_status_string.restype = ctypes.c_char_p
@@ -207,6 +213,28 @@ def mxq_fake_quantize_fp4_static(x, block_amax, global_amax, y, block_size,
                                             int(block_size), _ptr(block_amax),
                                             _ptr(global_amax), _ptr(y), _stream(x, stream)),
            "mxq_fake_quantize_fp4_static")
+
+
+def mxq_dequantize_kv_pages_nvfp4(values_ptrs, scales_ptrs, amax_ptrs, block_tokens, y,
+                                  stream=None) -> None:
+    """values_ptrs / scales_ptrs / amax_ptrs: int64 device tensors holding one
+    device address per cache block; y [blocks * block_tokens, heads, head_dim]
+    (a leading batch dim of 1 is allowed)."""
+    H, D = y.shape[-2], y.shape[-1]
+    nb = values_ptrs.numel()
+    _check(lib.mxq_dequantize_kv_pages_nvfp4(_ptr(values_ptrs), _ptr(scales_ptrs), _ptr(amax_ptrs),
+                                             nb, int(block_tokens), H, D, _ptr(y), _dt(y.dtype),
+                                             _stream(y, stream)),
+           "mxq_dequantize_kv_pages_nvfp4")
+
+
+def mxq_quantize_kv_nvfp4(k, head_amax, packed, scales, row_scale, smooth=True,
+                          stream=None) -> None:
+    S, H, D = k.shape[-3], k.shape[-2], k.shape[-1]
+    _check(lib.mxq_quantize_kv_nvfp4(_ptr(k), _dt(k.dtype), S, H, D, int(bool(smooth)),
+                                     _ptr(head_amax), _ptr(packed), _ptr(scales),
+                                     _ptr(row_scale), _stream(k, stream)),
+           "mxq_quantize_kv_nvfp4")
 
 
 # ------------------------------------------------------------------ tensor API
@@ -406,6 +434,63 @@ def fake_quantize_fp4_static(x: torch.Tensor, block_amax: torch.Tensor,
     y = torch.empty_like(xi)
     mxq_fake_quantize_fp4_static(xi, a, g, y, block_size)
     return y
+
+
+def _ptr_table(tensors, device) -> torch.Tensor:
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64).to(device)
+
+
+def dequantize_kv_cache(values, scales, amax, block_tokens: int, num_heads: int,
+                        dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Paged NVFP4 KV cache -> [1, blocks * block_tokens, num_heads, head_dim]
+    (LongLive's dequantize_kv_cache with row-major scale bytes): values[b]
+    uint8 [block_tokens * num_heads, head_dim // 2], scales[b] e4m3
+    [block_tokens * num_heads, head_dim // 16], amax[b] one float32, all on
+    the GPU; block b's global scale is amax[b] / (6 * 448)."""
+    nb = len(values)
+    if nb != len(scales) or nb != len(amax):
+        raise ValueError("values, scales and amax must list the same blocks")
+    if nb == 0:
+        raise ValueError("the cache holds no block")
+    D = values[0].shape[-1] * 2
+    rows = block_tokens * num_heads
+    for v, sc, a in zip(values, scales, amax):
+        if v.device.type != "cuda" or sc.device.type != "cuda" or a.device.type != "cuda":
+            raise ValueError("tensors must live on a GPU")
+        if (v.numel() != rows * D // 2 or sc.numel() != rows * D // 16 or a.numel() != 1
+                or not (v.is_contiguous() and sc.is_contiguous())
+                or v.data_ptr() % 16 or sc.data_ptr() % 16 or a.dtype != torch.float32):
+            raise ValueError("every block needs contiguous 16-byte aligned [rows, D/2] codes, "
+                             "[rows, D/16] scales and one float32 amax")
+    dev = values[0].device
+    y = torch.empty(1, nb * block_tokens, num_heads, D, dtype=dtype, device=dev)
+    vt, st, at = _ptr_table(values, dev), _ptr_table(scales, dev), _ptr_table(amax, dev)
+    mxq_dequantize_kv_pages_nvfp4(vt, st, at, block_tokens, y)
+    return y
+
+
+def quantize_kv_nvfp4(k: torch.Tensor, smooth: bool = True):
+    """Per-head NVFP4 of k [..., tokens, heads, head_dim] (LongLive's
+    quantize_kv with the default NVFP4 scale rule; smooth=True applies
+    k_smooth first).  Returns (uint8 packed [..., head_dim // 2], float8_e4m3fn
+    scales [..., head_dim // 16], float32 row scales [..., tokens, heads])."""
+    if k.dim() < 3:
+        raise ValueError("k must be [..., tokens, heads, head_dim]")
+    D = k.shape[-1]
+    if D < 16 or D > 512 or D & (D - 1):
+        raise ValueError("head_dim must be a power of two in [16, 512]")
+    x = _dev_input(k)
+    lead = tuple(x.shape[:-1])
+    S = x.numel() // (x.shape[-2] * D) if x.numel() else 0
+    packed = torch.empty(*lead, D // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(*lead, D // 16, dtype=torch.uint8, device=x.device)
+    row_scale = torch.empty(lead, dtype=torch.float32, device=x.device)
+    head_amax = torch.empty(x.shape[-2], dtype=torch.float32, device=x.device)
+    _check(lib.mxq_quantize_kv_nvfp4(_ptr(x), _dt(x.dtype), S, x.shape[-2], D, int(bool(smooth)),
+                                     _ptr(head_amax), _ptr(packed), _ptr(scales),
+                                     _ptr(row_scale), _stream(x)),
+           "mxq_quantize_kv_nvfp4")
+    return packed, scales.view(torch.float8_e4m3fn), row_scale
 
 
 def abi_version() -> int:

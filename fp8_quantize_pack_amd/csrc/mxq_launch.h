@@ -31,5 +31,12 @@ hipError_t launch_mxfp8_dequant(const uint8_t* codes, const uint8_t* scales,
 hipError_t launch_fp4_static_qdq(const void* x, int dt, int64_t rows, int64_t K,
                                  int block_size, const float* block_amax,
                                  const float* global_amax, void* y, hipStream_t s);
+hipError_t launch_kv_pages_dequant(const uint8_t* const* values, const uint8_t* const* scales,
+                                   const float* const* amax, int64_t nblocks,
+                                   int64_t block_tokens, int64_t H, int64_t D, void* y, int dt,
+                                   hipStream_t s);
+hipError_t launch_kv_quant(const void* k, int dt, int64_t S, int64_t H, int64_t D, int smooth,
+                           float* head_amax, uint8_t* packed, uint8_t* scales,
+                           float* row_scale, hipStream_t s);
 
 } // namespace mxq

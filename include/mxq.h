@@ -12,8 +12,9 @@
  *     mxfp4 or nvfp4 groups of any block size).
  *
  * Further calls: MXFP8 quantize / dequantize, static two-level FP4 fake
- * quantization with caller-given amax values, and the grouped GEMM over
- * packed fp4 expert weights.
+ * quantization with caller-given amax values, the NVFP4 KV cache (paged
+ * dequantization, per-head quantization with k_smooth), and the grouped
+ * GEMM over packed fp4 expert weights.
  *
  * Sources, cited by page title and section:
  *   [mxfp4 page] "nemo_automodel.components.quantization.mxfp4"
@@ -21,6 +22,8 @@
  *   [cache page] "nemo_automodel.components.models.deepseek_v41.quantization"
  *   [modelopt]   Model-Optimizer "tensor_quantizer.py" (TensorQuantizer,
  *                StaticBlockScaleQuantizer)
+ *   [longlive]   LongLive "utils/quant.py" (dequantize_kv_cache, k_smooth,
+ *                quantize_kv)
  *
  * Conventions shared by every call
  *   - Every data pointer is a DEVICE pointer to contiguous row-major memory
@@ -235,6 +238,57 @@ mxq_status mxq_fake_quantize_fp4_static(const void* x, mxq_dtype dt, int64_t row
                                         const float* block_amax,
                                         const float* global_amax, void* y,
                                         hipStream_t stream);
+
+/*
+ * Paged NVFP4 KV cache -> one contiguous tensor ([longlive] dequantize_kv_cache).
+ *   The cache is a list of num_blocks blocks, each a separate device
+ *   allocation reached through three DEVICE arrays of num_blocks DEVICE
+ *   pointers:
+ *     values[b]  uint8 [block_tokens * heads, head_dim / 2]: packed e2m1 codes,
+ *                row t * heads + h holding token t, head h;
+ *     scales[b]  e4m3 bytes [block_tokens * heads, head_dim / 16], row-major
+ *                (the page's third-party class keeps them swizzled; that
+ *                layout is not supported);
+ *     amax[b]    one float32: the block's global scale is amax / (6 * 448).
+ *   Each block's arrays must be 16-byte aligned.  head_dim % 16 == 0 (else
+ *   MXQ_E_SHAPE).
+ *   y  [num_blocks * block_tokens, heads, head_dim] of ydt (16-byte aligned):
+ *      token b * block_tokens + t of y is token t of block b; values decode as
+ *      mxq_dequantize_nvfp4 does ((e2m1 * e4m3) * global in float32, one
+ *      rounding to ydt).
+ */
+mxq_status mxq_dequantize_kv_pages_nvfp4(const uint8_t* const* values,
+                                         const uint8_t* const* scales,
+                                         const float* const* amax, int64_t num_blocks,
+                                         int64_t block_tokens, int64_t heads,
+                                         int64_t head_dim, void* y, mxq_dtype ydt,
+                                         hipStream_t stream);
+
+/*
+ * Per-head NVFP4 quantization of a K or V tensor ([longlive] quantize_kv,
+ * k_smooth), with the NVFP4 rule of [nvfp4 page] quantize_nvfp4_modelopt
+ * applied to each head's slice.
+ *   k          [tokens, heads, head_dim] of dt (16-byte aligned); head_dim a
+ *              power of two in [16, 512], heads <= 4096 (else MXQ_E_SHAPE).
+ *   smooth     1: each row (token, head) first has its mean removed
+ *              (k_smooth): mean = binary32 pairwise sum over the row times
+ *              1 / head_dim, rounded to dt; value - mean evaluated in binary32
+ *              and rounded to dt.  0: no smoothing (values).  Else MXQ_E_MODE.
+ *   head_amax  [heads] float32 device scratch, overwritten with each head's
+ *              amax (of the smoothed values).
+ *   packed     uint8 [tokens, heads, head_dim / 2] (16-byte aligned),
+ *   scales     e4m3 bytes [tokens, heads, head_dim / 16],
+ *   row_scale  float32 [tokens, heads]: the head's g = amax / (6 * 448) on each
+ *              of its rows, so that mxq_dequantize_nvfp4 with rows =
+ *              tokens * heads decodes the result.
+ *   Block scales and codes as mxq_quantize_nvfp4 with that g.  The page's
+ *   mean-squared-error scale rule belongs to a third-party library and is not
+ *   offered.  Two passes over k (the per-head amax first).
+ */
+mxq_status mxq_quantize_kv_nvfp4(const void* k, mxq_dtype dt, int64_t tokens, int64_t heads,
+                                 int64_t head_dim, int32_t smooth, float* head_amax,
+                                 uint8_t* packed, uint8_t* scales, float* row_scale,
+                                 hipStream_t stream);
 
 /*
  * Grouped GEMM over packed fp4 expert weights, dequantized on the fly

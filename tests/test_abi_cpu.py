@@ -21,7 +21,8 @@ def test_header_declares_the_operations():
     for n in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
               "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_grouped_mm_mxfp4",
               "mxq_grouped_mm_nvfp4", "mxq_quantize_mxfp8", "mxq_dequantize_mxfp8",
-              "mxq_fake_quantize_fp4_static", "mxq_status_string", "mxq_abi_version"):
+              "mxq_fake_quantize_fp4_static", "mxq_dequantize_kv_pages_nvfp4",
+              "mxq_quantize_kv_nvfp4", "mxq_status_string", "mxq_abi_version"):
         assert n in names
 
 
@@ -133,6 +134,29 @@ def test_fp4_static_validation(L):
     assert f(FAKE, 1, 4, 64, 16, None, FAKE, FAKE, None) == 1
     assert f(FAKE + 4, 1, 4, 64, 16, FAKE, FAKE, FAKE, None) == 9
     assert f(None, 1, 0, 64, 16, None, None, None, None) == 0
+
+
+def test_kv_validation(L):
+    d, q = L.mxq_dequantize_kv_pages_nvfp4, L.mxq_quantize_kv_nvfp4
+    # values, scales, amax, nb, bt, H, D, y, ydt, stream
+    assert d(FAKE, FAKE, FAKE, 4, 16, 8, 120, FAKE, 1, None) == 2     # D % 16
+    assert d(FAKE, FAKE, FAKE, -1, 16, 8, 128, FAKE, 1, None) == 2
+    assert d(FAKE, FAKE, FAKE, 4, 16, 8, 128, FAKE, 7, None) == 3
+    assert d(None, FAKE, FAKE, 4, 16, 8, 128, FAKE, 1, None) == 1
+    assert d(FAKE, FAKE, None, 4, 16, 8, 128, FAKE, 1, None) == 1
+    assert d(FAKE, FAKE, FAKE, 4, 16, 8, 128, FAKE + 2, 1, None) == 9
+    assert d(FAKE, FAKE, FAKE, 1 << 30, 1 << 20, 1 << 10, 128, FAKE, 1, None) == 6
+    assert d(None, None, None, 0, 16, 8, 128, None, 1, None) == 0
+    # k, dt, S, H, D, smooth, head_amax, packed, scales, row_scale, stream
+    assert q(FAKE, 1, 64, 8, 96, 1, FAKE, FAKE, FAKE, FAKE, None) == 2   # not a power of two
+    assert q(FAKE, 1, 64, 8, 8, 1, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert q(FAKE, 1, 64, 8, 1024, 1, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert q(FAKE, 1, 64, 5000, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert q(FAKE, 1, 64, 8, 128, 2, FAKE, FAKE, FAKE, FAKE, None) == 8
+    assert q(FAKE, 9, 64, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert q(FAKE, 1, 64, 8, 128, 1, None, FAKE, FAKE, FAKE, None) == 1
+    assert q(FAKE + 4, 1, 64, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == 9
+    assert q(None, 1, 0, 8, 128, 1, None, None, None, None, None) == 0
 
 
 def test_status_strings(L):
