@@ -46,6 +46,8 @@ def parse():
                     help="experts of the sweep (256 is the full workload)")
     ap.add_argument("--no-gemm", action="store_true",
                     help="skip the grouped-GEMM measurement (not part of `value`)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the MXFP8 / static FP4 / KV-cache measurements (not part of `value`)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a torch negation over one 36-expert chunk "
                          "(reads and writes CALIBRATION_BYTES) for HBM counter calibration")
@@ -74,6 +76,10 @@ def measured_traffic(kernel: str, src_hash: str):
         return None
     m = re.search(rf"^{re.escape(kernel)}\s+traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
     return float(m.group(1)) if m else None
+
+
+def progress(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
 
 
 def main():
@@ -109,6 +115,7 @@ def main():
     cache_in = {c: synth.kv_cache(synth.SHAPES[c], seed=synth.SEEDS[c], device=dev) for c, _, _ in cache_cases}
     cache_out = {c: torch.empty_like(v) for c, v in cache_in.items()}
     torch.cuda.synchronize()
+    progress("inputs resident:", E, "experts")
 
     # ---------------- one step: list of (op name, bytes, callable) ----------------
     plan = []
@@ -150,6 +157,7 @@ def main():
         run_step(ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    progress(f"{args.steps} timed steps: {wall:.3f} s")
 
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
@@ -182,6 +190,9 @@ def main():
                 "avg_launch_us": ops[dom]["avg_launch_us"]}
 
     gemm = None if args.no_gemm else grouped_gemm(torch, mxq, dev, max(args.steps, 1))
+    progress("grouped GEMM measured" if gemm else "grouped GEMM skipped")
+    extra = None if args.no_extra else extra_ops(torch, mxq, synth, dev, x, y, max(args.steps, 1))
+    progress("extra ops measured" if extra else "extra ops skipped")
 
     if args.calibrate_copy:
         # a plain elementwise kernel of known traffic, outside the timed region
@@ -195,6 +206,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, args.cpu_seconds)
+        progress("CPU oracle baseline measured")
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -210,6 +222,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "grouped_gemm": gemm,
+        "extra_ops": extra,
         "ops": ops,
         "kernel_source_hash": src_hash,
     }
@@ -257,6 +270,81 @@ def grouped_gemm(torch, mxq, dev, reps):
             out[f"{fmt}_{'backward' if tr else 'forward'}"] = {
                 "experts": E, "N": N, "K": K, "tokens": T, "avg_launch_us": round(t * 1e6, 1),
                 "TFLOPs": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
+def _time_launches(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps * 1e-3
+
+
+def extra_ops(torch, mxq, synth, dev, x, y, reps):
+    """The other calls of the library, each timed with HIP events around
+    `reps` launches on resident inputs, with its algorithmic bytes (inputs
+    read once, outputs written once) and its fraction of the HBM peak; not
+    part of `value`.
+      * MXFP8 quantize / dequantize and the static two-level FP4 round trip
+        (block 16, calibrated block amax) on one 36-expert chunk of the sweep,
+        bf16 [36, 2048, 7168];
+      * the NVFP4 KV cache: per-head quantization with k_smooth of K
+        [32768, 12, 128] bf16 (two kernels: the per-head amax pass and the
+        quantize pass; its bytes count K read once), and the paged
+        dequantization of 32 cache blocks of 1024 tokens into
+        [32768, 12, 128] bf16."""
+    out = {"peak_GBps": PEAK_HBM_GBPS, "bound": "hbm"}
+
+    def record(name, nbytes, t, **kw):
+        gbps = nbytes / t / 1e9
+        out[name] = dict(kw, bytes_per_launch=int(nbytes), avg_launch_us=round(t * 1e6, 1),
+                         GBps=round(gbps, 1), frac=round(gbps / PEAK_HBM_GBPS, 4))
+
+    ne = synth.C5_CHUNK_EXPERTS
+    xs, ys = x[:ne], y[:ne]
+    n = xs.numel()
+    K = xs.shape[-1]
+    codes = torch.empty(xs.shape, dtype=torch.uint8, device=dev)
+    sc8 = torch.empty((*xs.shape[:-1], K // 32), dtype=torch.uint8, device=dev)
+    b8 = 2 * n + n + n // 32
+    record("mxfp8_quant", b8, _time_launches(torch, lambda: mxq.mxq_quantize_mxfp8(xs, codes, sc8), reps),
+           shape=list(xs.shape))
+    record("mxfp8_dequant", b8, _time_launches(torch, lambda: mxq.mxq_dequantize_mxfp8(codes, sc8, ys), reps),
+           shape=list(xs.shape))
+    del codes, sc8
+    amax = xs.abs().reshape(-1, K // 16, 16).amax(-1).float()    # calibrated block amax
+    gam = xs.abs().max().float().reshape(1)
+    bst = 2 * n + 2 * n + 4 * (n // 16) + 4
+    record("fp4_static_qdq", bst,
+           _time_launches(torch, lambda: mxq.mxq_fake_quantize_fp4_static(xs, amax, gam, ys, 16), reps),
+           shape=list(xs.shape), block=16)
+    del amax
+    S, H, D, bt = 32768, 12, 128, 1024
+    k = synth.kv_cache((S, H, D), seed=5, device=dev)
+    kp = torch.empty((S, H, D // 2), dtype=torch.uint8, device=dev)
+    ks = torch.empty((S, H, D // 16), dtype=torch.uint8, device=dev)
+    kg = torch.empty((S, H), dtype=torch.float32, device=dev)
+    ha = torch.empty(H * mxq.KV_AMAX_SLOTS, dtype=torch.float32, device=dev)
+    nk = k.numel()
+    bkv = 2 * nk + nk // 2 + nk // 16 + 4 * S * H
+    record("kv_quantize_smooth", bkv,
+           _time_launches(torch, lambda: mxq.mxq_quantize_kv_nvfp4(k, ha, kp, ks, kg, True), reps),
+           shape=[S, H, D])
+    nb = S // bt
+    blocks = [(kp.reshape(nb, bt * H, D // 2)[b].clone(), ks.reshape(nb, bt * H, D // 16)[b].clone(),
+               ha[::mxq.KV_AMAX_SLOTS].max().reshape(1).clone()) for b in range(nb)]
+    tab = lambda i: torch.tensor([blk[i].data_ptr() for blk in blocks], dtype=torch.int64).to(dev)
+    vt, st, at = tab(0), tab(1), tab(2)
+    yk = torch.empty((S, H, D), dtype=torch.bfloat16, device=dev)
+    bpg = nk // 2 + nk // 16 + 4 * nb + 2 * nk
+    record("kv_pages_dequant", bpg,
+           _time_launches(torch, lambda: mxq.mxq_dequantize_kv_pages_nvfp4(vt, st, at, bt, yk), reps),
+           blocks=nb, block_tokens=bt, heads=H, head_dim=D)
     return out
 
 

@@ -385,6 +385,7 @@ def grouped_mm_nvfp4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
 
 
 MXFP8_BLOCK_SIZE = 32
+KV_AMAX_SLOTS = 32          # scratch words per head of mxq_quantize_kv_nvfp4
 
 
 def quantize_mxfp8(weight: torch.Tensor):
@@ -485,7 +486,7 @@ def quantize_kv_nvfp4(k: torch.Tensor, smooth: bool = True):
     packed = torch.empty(*lead, D // 2, dtype=torch.uint8, device=x.device)
     scales = torch.empty(*lead, D // 16, dtype=torch.uint8, device=x.device)
     row_scale = torch.empty(lead, dtype=torch.float32, device=x.device)
-    head_amax = torch.empty(x.shape[-2], dtype=torch.float32, device=x.device)
+    head_amax = torch.empty(x.shape[-2] * KV_AMAX_SLOTS, dtype=torch.float32, device=x.device)
     _check(lib.mxq_quantize_kv_nvfp4(_ptr(x), _dt(x.dtype), S, x.shape[-2], D, int(bool(smooth)),
                                      _ptr(head_amax), _ptr(packed), _ptr(scales),
                                      _ptr(row_scale), _stream(x)),

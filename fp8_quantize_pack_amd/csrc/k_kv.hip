@@ -13,13 +13,14 @@
 // through device arrays of pointers (the cache's block list); block b lands at
 // tokens b * block_tokens .. of the output [blocks * block_tokens, H, D], so
 // the output is the blocks' rows concatenated.  Each wavefront owns a tile of
-// 2 x 64 consecutive 8-element chunks of one block: it reads the block's
-// pointers and amax once (uniform), a packed dword and a scale byte per lane,
-// and writes 16 bytes (bfloat16) per lane, contiguous over the wave.
+// 8 x 64 consecutive 8-element chunks of one block: it reads the block's
+// pointers and amax once (uniform), then per step a packed dword and a scale
+// byte per lane, and writes 16 bytes (bfloat16) per lane, contiguous over the
+// wave.
 //
 // Quantization with k_smooth.  k [S, H, D], D a power of two in [16, 512].
 // Each row (token, head) of D values is optionally smoothed: its mean is the
-// binary32 pairwise sum (8 values in a lane, then a butterfly over the D / 8
+// binary32 pairwise sum (16 values in a lane, then a butterfly over the D / 16
 // lanes of the row: the pairwise tree, since every addition is commutative)
 // times 1 / D, rounded to the dtype; each value minus that mean is evaluated
 // in binary32 and rounded to the dtype.  Every head's slice then gets one
@@ -27,8 +28,10 @@
 // Pass 1 reduces the per-head maxima of the (smoothed) values: each
 // workgroup owns a contiguous range of rows, folds them into per-head maxima
 // in LDS, then issues one global atomic maximum per head; pass 2 recomputes
-// the smoothed values (deterministic) and quantizes.  Rows are contiguous
-// in memory, so every load and store of a wave is one contiguous range.
+// the smoothed values (deterministic) and quantizes, one binary64 block
+// reciprocal per lane and 16 values (lane pairs share blocks, as in the
+// NVFP4 row kernel).  Every load and store instruction of a wave covers one
+// contiguous range.
 #include "mxq_kernel_common.h"
 #include "mxq_launch.h"
 #include "mxq_nvfp4_common.h"
@@ -37,8 +40,18 @@ namespace mxq {
 
 // ------------------------------------------------------------------ paged dequantization
 
-constexpr int kKvUnroll = 2;
+// 8 x 64 chunks per wave tile: 4 KiB of codes and 16 KiB of bfloat16 output
+// per wave, so that the two dependent loads of the block's pointers and amax
+// are amortized and enough loads are in flight.
+#ifndef MXQ_KV_PAGE_UNROLL
+#define MXQ_KV_PAGE_UNROLL 8
+#endif
+constexpr int kKvUnroll = MXQ_KV_PAGE_UNROLL;
 constexpr int kKvTileChunks = kKvUnroll * kWave;
+
+typedef const uint32_t __attribute__((address_space(1))) GlobalU32;
+typedef const uint8_t __attribute__((address_space(1))) GlobalU8;
+typedef const float __attribute__((address_space(1))) GlobalF32;
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_kv_pages_dequant(
@@ -51,15 +64,17 @@ __global__ __launch_bounds__(256) void k_kv_pages_dequant(
        t += nwaves) {
     const int64_t b = t / tiles_per_block;                 // uniform over the wave
     const int64_t c0 = (t - b * tiles_per_block) * kKvTileChunks + lane;
-    const uint32_t* vb = reinterpret_cast<const uint32_t*>(values[b]);
-    const uint8_t* sb = scales[b];
-    const float g = *amax[b] / kGlobalDiv;
+    // pointers read from memory are generic; the block arrays live in global
+    // memory, so address them as such (global rather than flat loads)
+    const GlobalU32* vb = (const GlobalU32*)(values[b]);
+    const GlobalU8* sb = (const GlobalU8*)(scales[b]);
+    const float g = *(const GlobalF32*)(amax[b]) / kGlobalDiv;
     uint32_t w[kKvUnroll], s[kKvUnroll];
 #pragma unroll
     for (int u = 0; u < kKvUnroll; ++u) {
       const int64_t c = c0 + u * kWave;
       const bool ok = c < cpb;
-      w[u] = ok ? stream_ld(vb + c) : 0u;
+      w[u] = ok ? __builtin_nontemporal_load(vb + c) : 0u;
       s[u] = ok ? (uint32_t)sb[c >> 1] : 0u;
     }
 #pragma unroll
@@ -101,6 +116,7 @@ hipError_t launch_kv_pages_dequant(const uint8_t* const* values, const uint8_t* 
 // holds identically).
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
+  // G == 1: the lane holds the whole row
   if constexpr (G >= 2) x = x + bitsf(dpp_u32<0xB1>(fbits(x)));    // lane ^ 1
   if constexpr (G >= 4) x = x + bitsf(dpp_u32<0x4E>(fbits(x)));    // lane ^ 2
   if constexpr (G >= 8) x = x + bitsf(dpp_u32<0x141>(fbits(x)));   // other quad of 8
@@ -112,112 +128,209 @@ __device__ __forceinline__ float group_sum(float x) {
 
 template <int DT>
 __device__ __forceinline__ float round_to_dt(float v) {
-  if constexpr (DT == DT_BF16) return bitsf(f32_to_bf16_rne(v) << 16);
+  if constexpr (DT == DT_BF16) return bitsf(bf16x2_rne(v, 0.0f) << 16);
   else if constexpr (DT == DT_F16) return f16_to_f32(f32_to_f16_rne(v));
   else return v;
 }
 
-// k - mean(k) of the 8 values of this lane; the row spans L lanes.  Every
-// lane of the wave must call this together.
+// k - mean(k) of the 8 values of this lane; the row spans L lanes (L
+// consecutive chunks).  Every lane of the wave must call this together.  The
+// in-lane sum is the pairwise tree over the 8 values and the lanes continue
+// it.  bfloat16 rounds through the hardware pair converter (round to nearest
+// even, two values per instruction); each difference is a float32 value
+// first.
 template <int DT, int L>
 __device__ __forceinline__ void k_smooth8(float f[8]) {
   float s = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
   s = group_sum<L>(s);
   const float m = round_to_dt<DT>(s * (1.0f / (float)(8 * L)));   // exact scaling
+  if constexpr (DT == DT_BF16) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = round_to_dt<DT>(f[i] - m);
+    for (int i = 0; i < 8; i += 2) {
+      const float d0 = f[i] - m, d1 = f[i + 1] - m;
+      unpack_bf16x2(bf16x2_rne(d0, d1), f[i], f[i + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = round_to_dt<DT>(f[i] - m);
+  }
 }
 
+// Work layout of both passes: a wavefront tile is 128 consecutive chunks of
+// 8 values; lane l holds chunks l and 64 + l, so each of the two load (and
+// store) instructions covers one contiguous 1 KiB (bfloat16) range.  A row of
+// D values is L = D / 8 consecutive chunks and never straddles the two
+// halves (L divides 64); the 16-value blocks are lane pairs.  The grid is a
+// fixed number of workgroups whose waves stride over the tiles, so that each
+// workgroup's set-up (LDS tables, the final atomics) is paid once.
+#ifndef MXQ_KV_GRID_BLOCKS
+#define MXQ_KV_GRID_BLOCKS 1024
+#endif
+constexpr int64_t kKvGridBlocks = MXQ_KV_GRID_BLOCKS;
+#ifndef MXQ_KV_ROW_UNROLL
+#define MXQ_KV_ROW_UNROLL 4
+#endif
+constexpr int kKvRowUnroll = MXQ_KV_ROW_UNROLL;        // tiles in flight per wave
+
 struct KvGeom {
-  int64_t rows;      // S * H
-  int64_t rows_per_block;
+  int64_t nchunks;   // S * H * D / 8
+  int64_t tiles;     // ceil(nchunks / 128)
   int H;
 };
 
-// Rows of this lane in iteration it of workgroup blk: a contiguous run of
-// rows_per_block rows per workgroup, 4 waves x (64 / L) rows per iteration.
+// Each head's maximum is spread over kKvAmaxSlots words (workgroup b folds
+// into slot b % kKvAmaxSlots), which keeps the atomics on one address few.
+constexpr int kKvAmaxSlots = 32;
+
+// Tile, rows and heads of this lane's two chunks, advanced by the wave stride.
 template <int L>
-__device__ __forceinline__ int64_t kv_row(const KvGeom& geo, int it) {
-  constexpr int kRpw = 64 / L;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  return (int64_t)blockIdx.x * geo.rows_per_block + (int64_t)it * (4 * kRpw) + wave * kRpw + lane / L;
+struct KvRows {
+  int64_t tile;       // current tile of this wave
+  int64_t stride;     // waves in the grid
+  int64_t row_a;      // row of chunk l; the row of chunk 64 + l is row_a + 64 / L
+  uint32_t h_a, h_b;
+  uint32_t step;      // head advance per stride
+  __device__ __forceinline__ KvRows(const KvGeom& geo) {
+    constexpr int R = 128 / L;                           // rows per tile
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    tile = (int64_t)blockIdx.x * 4 + wave;
+    stride = (int64_t)gridDim.x * 4;
+    row_a = tile * R + lane / L;
+    h_a = (uint32_t)(row_a % geo.H);
+    h_b = (uint32_t)((row_a + R / 2) % geo.H);
+    step = (uint32_t)((stride * R) % geo.H);
+  }
+  __device__ __forceinline__ void advance(int H) {
+    tile += stride;
+    row_a += stride * (128 / L);
+    h_a += step; h_a = h_a >= (uint32_t)H ? h_a - H : h_a;
+    h_b += step; h_b = h_b >= (uint32_t)H ? h_b - H : h_b;
+  }
+};
+
+template <int DT>
+struct KvTile { Raw8<DT> c0, c1; };
+
+template <int DT>
+__device__ __forceinline__ KvTile<DT> kv_tile_load(const void* k, const KvGeom& geo, int64_t tile) {
+  const int64_t c = tile * 128 + (threadIdx.x & 63);
+  KvTile<DT> t;
+  t.c0 = c < geo.nchunks ? ld8<DT>(k, c) : zero8<DT>();
+  t.c1 = c + 64 < geo.nchunks ? ld8<DT>(k, c + 64) : zero8<DT>();
+  return t;
 }
 
 template <int DT, bool SMOOTH, int L>
 __global__ __launch_bounds__(256) void k_kv_head_amax(const void* __restrict__ k, KvGeom geo,
                                                       uint32_t* __restrict__ head_amax) {
   extern __shared__ uint32_t s_max[];
-  constexpr int kRpw = 64 / L;
+  constexpr int U = kKvRowUnroll;
   for (int i = threadIdx.x; i < geo.H; i += blockDim.x) s_max[i] = 0u;
   __syncthreads();
-  const int sub = threadIdx.x & (L - 1);
-  const int64_t end0 = (int64_t)blockIdx.x * geo.rows_per_block + geo.rows_per_block;
-  const int64_t end = end0 < geo.rows ? end0 : geo.rows;
-  const int iters = (int)((geo.rows_per_block + 4 * kRpw - 1) / (4 * kRpw));
-  const int64_t r0 = kv_row<L>(geo, 0);
-  uint32_t h = (uint32_t)(r0 % geo.H);
-  const uint32_t step = (uint32_t)((4 * kRpw) % geo.H);
-  for (int it = 0; it < iters; ++it) {
-    const int64_t row = r0 + (int64_t)it * (4 * kRpw);
-    const bool ok = row < end;
-    const Raw8<DT> raw = ok ? ld8<DT>(k, row * L + sub) : zero8<DT>();
-    float f[8];
-    unpack8<DT>(raw, f);
-    if constexpr (SMOOTH) k_smooth8<DT, L>(f);
-    float a = 0.0f;
+  const bool first = (threadIdx.x & (L - 1)) == 0;      // first lane of its row
+  KvRows<L> rr(geo);
+  while (rr.tile < geo.tiles) {                          // uniform over the wave
+    KvTile<DT> t[U];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-    a = group_max<L>(a);
-    if (ok && sub == 0) atomicMax(&s_max[h], fbits(a));
-    h += step;
-    h = h >= (uint32_t)geo.H ? h - geo.H : h;
+    for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT>(k, geo, rr.tile + u * rr.stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = rr.tile * 128 + (threadIdx.x & 63);
+      float f0[8], f1[8];
+      unpack8<DT>(t[u].c0, f0);
+      unpack8<DT>(t[u].c1, f1);
+      if constexpr (SMOOTH) {
+        k_smooth8<DT, L>(f0);
+        k_smooth8<DT, L>(f1);
+      }
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        a0 = fmaxf(a0, fabsf(f0[i]));
+        a1 = fmaxf(a1, fabsf(f1[i]));
+      }
+      a0 = group_max<L>(a0);
+      a1 = group_max<L>(a1);
+      if (first && c < geo.nchunks) atomicMax(&s_max[rr.h_a], fbits(a0));
+      if (first && c + 64 < geo.nchunks) atomicMax(&s_max[rr.h_b], fbits(a1));
+      rr.advance(geo.H);
+    }
   }
   __syncthreads();
+  const int slot = blockIdx.x % kKvAmaxSlots;
   for (int i = threadIdx.x; i < geo.H; i += blockDim.x)
-    if (s_max[i] != 0u) atomicMax(&head_amax[i], s_max[i]);
+    if (s_max[i] != 0u) atomicMax(&head_amax[i * kKvAmaxSlots + slot], s_max[i]);
 }
 
 template <int DT, bool SMOOTH, int L>
 __global__ __launch_bounds__(256) void k_kv_quant(const void* __restrict__ k, KvGeom geo,
-                                                  const uint32_t* __restrict__ head_amax,
+                                                  uint32_t* __restrict__ head_amax,
                                                   uint32_t* __restrict__ packed,
                                                   uint8_t* __restrict__ scales,
                                                   float* __restrict__ row_scale) {
-  constexpr int kRpw = 64 / L;
-  const int sub = threadIdx.x & (L - 1);
-  const int64_t end0 = (int64_t)blockIdx.x * geo.rows_per_block + geo.rows_per_block;
-  const int64_t end = end0 < geo.rows ? end0 : geo.rows;
-  const int iters = (int)((geo.rows_per_block + 4 * kRpw - 1) / (4 * kRpw));
-  const int64_t r0 = kv_row<L>(geo, 0);
-  uint32_t h = (uint32_t)(r0 % geo.H);
-  const uint32_t step = (uint32_t)((4 * kRpw) % geo.H);
-  for (int it = 0; it < iters; ++it) {
-    const int64_t row = r0 + (int64_t)it * (4 * kRpw);
-    const bool ok = row < end;
-    const Raw8<DT> raw = ok ? ld8<DT>(k, row * L + sub) : zero8<DT>();
-    float f[8];
-    unpack8<DT>(raw, f);
-    if constexpr (SMOOTH) k_smooth8<DT, L>(f);
-    // the 16-value block of this chunk is shared with lane ^ 1
-    float a = 0.0f;
+  // per-head amax (the maximum over its slots; workgroup 0 writes it back to
+  // slot 0, which leaves every reader's maximum unchanged), g = amax / 2688
+  // and its correctly rounded binary64 reciprocal
+  extern __shared__ double s_rg[];
+  float* s_g = reinterpret_cast<float*>(s_rg + geo.H);
+  for (int i = threadIdx.x; i < geo.H; i += blockDim.x) {
+    uint32_t m = 0u;
+    for (int j = 0; j < kKvAmaxSlots; ++j) m = max(m, head_amax[i * kKvAmaxSlots + j]);
+    if (blockIdx.x == 0) head_amax[i * kKvAmaxSlots] = m;
+    const float g = bitsf(m) / kGlobalDiv;
+    s_g[i] = g;
+    s_rg[i] = 1.0 / (double)g;
+  }
+  __syncthreads();
+  constexpr int U = kKvRowUnroll;
+  const int lane = threadIdx.x & 63;
+  const bool odd = lane & 1;
+  const bool first = (lane & (L - 1)) == 0;
+  KvRows<L> rr(geo);
+  while (rr.tile < geo.tiles) {                          // uniform over the wave
+    KvTile<DT> t[U];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-    a = bitsf(max(fbits(a), pair_swap(fbits(a))));
-    const float g = bitsf(head_amax[h]) / kGlobalDiv;
-    const double rg = 1.0 / (double)g;
-    uint32_t sb;
-    const double rden = nv_block_recip(a, g, rg, sb);
-    float q[8];
+    for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT>(k, geo, rr.tile + u * rr.stride);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f[i] * rden));
-    const uint32_t w = e2m1_pack8_rne(q, 1.0f);
-    if (ok) {
-      stream_st(w, packed + row * L + sub);
-      if ((sub & 1) == 0) scales[row * (L / 2) + (sub >> 1)] = (uint8_t)sb;
-      if (sub == 0) row_scale[row] = g;
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = rr.tile * 128 + lane;
+      float f0[8], f1[8];
+      unpack8<DT>(t[u].c0, f0);
+      unpack8<DT>(t[u].c1, f1);
+      if constexpr (SMOOTH) {
+        k_smooth8<DT, L>(f0);
+        k_smooth8<DT, L>(f1);
+      }
+      // block maxima of both chunks (the block is this lane pair); the even
+      // lane takes the scale of chunk 0's block, the odd lane that of chunk 1's
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        a0 = fmaxf(a0, fabsf(f0[i]));
+        a1 = fmaxf(a1, fabsf(f1[i]));
+      }
+      a0 = bitsf(max(fbits(a0), pair_swap(fbits(a0))));
+      a1 = bitsf(max(fbits(a1), pair_swap(fbits(a1))));
+      const uint32_t hm = odd ? rr.h_b : rr.h_a;
+      uint32_t sb;
+      const double mine = nv_block_recip(odd ? a1 : a0, s_g[hm], s_rg[hm], sb);
+      const double other = pair_swap(mine);
+      const double r0 = odd ? other : mine, r1 = odd ? mine : other;
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f0[i] * r0));
+      const uint32_t w0 = e2m1_pack8_rne(q, 1.0f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f1[i] * r1));
+      const uint32_t w1 = e2m1_pack8_rne(q, 1.0f);
+      const int64_t cm = odd ? c + 64 : c;                // chunk of this lane's block
+      if (c < geo.nchunks) stream_st(w0, packed + c);
+      if (c + 64 < geo.nchunks) stream_st(w1, packed + c + 64);
+      if (cm < geo.nchunks) scales[cm >> 1] = (uint8_t)sb;
+      if (first && c < geo.nchunks) row_scale[rr.row_a] = s_g[rr.h_a];
+      if (first && c + 64 < geo.nchunks) row_scale[rr.row_a + 64 / L] = s_g[rr.h_b];
+      rr.advance(geo.H);
     }
-    h += step;
-    h = h >= (uint32_t)geo.H ? h - geo.H : h;
   }
 }
 
@@ -230,17 +343,18 @@ template <int DT, bool SMOOTH, int L>
 static void launch_kv_quant_l(const void* k, const KvGeom& geo, int64_t nblk,
                               uint32_t* head_amax, uint32_t* packed, uint8_t* scales,
                               float* row_scale, hipStream_t s) {
-  const size_t lds = sizeof(uint32_t) * (size_t)geo.H;
-  hipLaunchKernelGGL((k_kv_head_amax<DT, SMOOTH, L>), dim3((unsigned)nblk), dim3(256), lds, s, k,
-                     geo, head_amax);
-  hipLaunchKernelGGL((k_kv_quant<DT, SMOOTH, L>), dim3((unsigned)nblk), dim3(256), 0, s, k, geo,
-                     head_amax, packed, scales, row_scale);
+  const size_t lds_max = sizeof(uint32_t) * (size_t)geo.H;
+  const size_t lds_g = (sizeof(double) + sizeof(float)) * (size_t)geo.H;
+  hipLaunchKernelGGL((k_kv_head_amax<DT, SMOOTH, L>), dim3((unsigned)nblk), dim3(256), lds_max, s,
+                     k, geo, head_amax);
+  hipLaunchKernelGGL((k_kv_quant<DT, SMOOTH, L>), dim3((unsigned)nblk), dim3(256), lds_g, s, k,
+                     geo, head_amax, packed, scales, row_scale);
 }
 
 template <int DT, bool SMOOTH>
 static void launch_kv_quant_d(const void* k, const KvGeom& geo, int64_t nblk, int64_t D,
                               uint32_t* ha, uint32_t* p, uint8_t* sc, float* rs, hipStream_t s) {
-  switch (D) {
+  switch (D) {     // chunks (lanes) per row
     case 16: launch_kv_quant_l<DT, SMOOTH, 2>(k, geo, nblk, ha, p, sc, rs, s); break;
     case 32: launch_kv_quant_l<DT, SMOOTH, 4>(k, geo, nblk, ha, p, sc, rs, s); break;
     case 64: launch_kv_quant_l<DT, SMOOTH, 8>(k, geo, nblk, ha, p, sc, rs, s); break;
@@ -258,20 +372,18 @@ static void launch_kv_quant_dt(const void* k, const KvGeom& geo, int64_t nblk, i
   else launch_kv_quant_d<DT, false>(k, geo, nblk, D, ha, p, sc, rs, s);
 }
 
-// Rows per workgroup: enough that the per-head atomics stay few, small
-// enough that the grid has several workgroups per CU.
-constexpr int64_t kKvRowsPerBlock = 512;
-
 hipError_t launch_kv_quant(const void* k, int dt, int64_t S, int64_t H, int64_t D, int smooth,
                            float* head_amax, uint8_t* packed, uint8_t* scales,
                            float* row_scale, hipStream_t s) {
   KvGeom geo;
-  geo.rows = S * H;
+  geo.nchunks = S * H * (D / 8);
+  geo.tiles = (geo.nchunks + 127) / 128;
   geo.H = (int)H;
-  geo.rows_per_block = kKvRowsPerBlock;
-  const int64_t nblk = (geo.rows + kKvRowsPerBlock - 1) / kKvRowsPerBlock;
+  int64_t nblk = (geo.tiles + 3) / 4;
+  nblk = nblk < kKvGridBlocks ? nblk : kKvGridBlocks;
   uint32_t* ha = reinterpret_cast<uint32_t*>(head_amax);
-  hipLaunchKernelGGL(k_fill_head_amax, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, s, ha, (int)H);
+  const int nslots = (int)H * kKvAmaxSlots;
+  hipLaunchKernelGGL(k_fill_head_amax, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, ha, nslots);
   uint32_t* p = reinterpret_cast<uint32_t*>(packed);
   switch (dt) {
     case DT_F32: launch_kv_quant_dt<DT_F32>(k, geo, nblk, D, smooth != 0, ha, p, scales, row_scale, s); break;

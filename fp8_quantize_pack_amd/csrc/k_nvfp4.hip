@@ -219,80 +219,86 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_short(
 // Whole-tensor amax for the one-tensor-scale mode: a grid-stride max over all
 // chunks, reduced per wave and combined with an integer atomic max on the bit
 // patterns (non-negative floats order like their patterns).
+// Whole-tensor amax: a grid-stride pass with four chunks in flight per lane
+// (magnitude maxima on the raw 16-bit patterns), one atomic maximum per wave.
 template <int DT>
 __global__ __launch_bounds__(256) void k_tensor_amax(const void* __restrict__ x,
                                                      int64_t nchunks,
                                                      uint32_t* __restrict__ out) {
-  float amax = 0.0f;
+  uint32_t m = 0u;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
-    float f[8];
-    unpack8<DT>(ld8<DT>(x, c), f);
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; c + 3 * stride < nchunks; c += 4 * stride) {
+    Raw8<DT> r[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    for (int u = 0; u < 4; ++u) r[u] = ld8<DT>(x, c + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = max(m, amax8_bits<DT>(r[u]));
   }
-  amax = group_max<64>(amax);
+  for (; c < nchunks; c += stride) m = max(m, amax8_bits<DT>(ld8<DT>(x, c)));
+  const float amax = group_max<64>(amax_from_bits<DT>(m));
   if ((threadIdx.x & 63) == 0) atomicMax(out, fbits(amax));
 }
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
-// Dequantization of short rows (fewer than kDqSegChunks chunks) works on
-// 8-element chunks (one packed dword, half a block) so that every load and
-// store instruction of a wavefront is contiguous: lane `sub` of a row owns the
-// chunks sub, sub + LPR, ..., kDqUnroll of them in flight at a time, 64 / LPR
-// rows per wave.
-struct NvChunkGeom {
-  int64_t rows;
-  int64_t cpr;      // 8-element chunks per row = K / 8
-  int lpr;          // lanes per row (>= 2, a power of two)
-  int niter;        // ceil(cpr / lpr)
+// Dequantization of short rows (fewer than kDqSegChunks chunks): the tensor
+// is a flat run of 8-element chunks (rows are contiguous and hold an even
+// number of chunks, so chunk c's scale byte is c / 2).  A wavefront owns
+// kDqFlatUnroll x 64 consecutive chunks, every load and store instruction
+// contiguous over the wave; each lane finds the row of its first chunk with
+// one division and advances it by a fixed quotient and remainder per step.
+#ifndef MXQ_NVD_FLAT_UNROLL
+#define MXQ_NVD_FLAT_UNROLL 8
+#endif
+constexpr int kDqFlatUnroll = MXQ_NVD_FLAT_UNROLL;
+constexpr int kDqFlatTile = kDqFlatUnroll * kWave;
+
+struct NvFlatGeom {
+  int64_t nchunks;
+  int64_t cpr;      // chunks per row (even, < kDqSegChunks)
+  int64_t ntiles;
+  int32_t drow;     // 64 / cpr
+  int32_t drem;     // 64 % cpr
 };
 
-#ifndef MXQ_NVD_UNROLL
-#define MXQ_NVD_UNROLL 16
-#endif
-constexpr int kDqUnroll = MXQ_NVD_UNROLL;
-
 template <int DT>
-__global__ __launch_bounds__(256) void k_nvfp4_dequant(
+__global__ __launch_bounds__(256) void k_nvfp4_dequant_flat(
     const uint32_t* __restrict__ packed, const uint8_t* __restrict__ scales,
-    const float* __restrict__ row_scale, NvChunkGeom geo, void* __restrict__ y) {
+    const float* __restrict__ row_scale, NvFlatGeom geo, void* __restrict__ y) {
   const int lane = threadIdx.x & 63;
-  const int sub = lane & (geo.lpr - 1);
-  const int rows_per_wave = kWave / geo.lpr;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int64_t ngroups = (geo.rows + rows_per_wave - 1) / rows_per_wave;
-  for (int64_t wg = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-       wg < ngroups; wg += nwaves) {
-    const int64_t row = wg * rows_per_wave + lane / geo.lpr;
-    if (row >= geo.rows) continue;
-    const int64_t rbase = row * geo.cpr;
-    const float g = row_scale[row];
-    for (int it0 = 0; it0 < geo.niter; it0 += kDqUnroll) {
-      uint32_t w[kDqUnroll], sb[kDqUnroll];
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < geo.ntiles;
+       t += nwaves) {
+    const int64_t c0 = t * kDqFlatTile + lane;
+    int64_t row = c0 / geo.cpr;
+    int32_t rem = (int32_t)(c0 - row * geo.cpr);
+    uint32_t w[kDqFlatUnroll], sb[kDqFlatUnroll];
+    float g[kDqFlatUnroll];
 #pragma unroll
-      for (int u = 0; u < kDqUnroll; ++u) {
-        const int64_t j = sub + (int64_t)(it0 + u) * geo.lpr;
-        const bool ok = j < geo.cpr;
-        w[u] = ok ? stream_ld(packed + rbase + j) : 0u;
-        sb[u] = ok ? (uint32_t)scales[(rbase + j) >> 1] : 0u;
+    for (int u = 0; u < kDqFlatUnroll; ++u) {
+      const int64_t c = c0 + u * kWave;
+      const bool ok = c < geo.nchunks;
+      w[u] = ok ? stream_ld(packed + c) : 0u;
+      sb[u] = ok ? (uint32_t)scales[c >> 1] : 0u;
+      g[u] = ok ? row_scale[row] : 0.0f;
+      row += geo.drow;
+      rem += geo.drem;
+      if (rem >= geo.cpr) { rem -= (int32_t)geo.cpr; ++row; }
+    }
+#pragma unroll
+    for (int u = 0; u < kDqFlatUnroll; ++u) {
+      const int64_t c = c0 + u * kWave;
+      float f[8];
+      if constexpr (DT == DT_F16) {
+        nvfp4_dequant8(w[u], sb[u], g[u], f);
+      } else {
+        const float sigma = e4m3_decode_any(sb[u]);
+        e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g[u];     // exact, then RN
       }
-#pragma unroll
-      for (int u = 0; u < kDqUnroll; ++u) {
-        const int64_t j = sub + (int64_t)(it0 + u) * geo.lpr;
-        if (j >= geo.cpr) continue;
-        float f[8];
-        if constexpr (DT == DT_F16) {
-          nvfp4_dequant8(w[u], sb[u], g, f);
-        } else {
-          const float sigma = e4m3_decode_any(sb[u]);
-          e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g;        // exact, then RN
-        }
-        st8<DT>(y, rbase + j, f);
-      }
+      if (c < geo.nchunks) st8<DT>(y, c, f);
     }
   }
 }
@@ -463,20 +469,18 @@ hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales,
     }
     return hipGetLastError();
   }
-  NvChunkGeom geo;
-  geo.rows = rows;
+  NvFlatGeom geo;
+  geo.nchunks = rows * cpr;
   geo.cpr = cpr;
-  int lpr = 2;
-  while (lpr < 64 && lpr < geo.cpr) lpr <<= 1;
-  geo.lpr = lpr;
-  geo.niter = (int)((geo.cpr + lpr - 1) / lpr);
-  const int64_t waves = (rows + (kWave / lpr) - 1) / (kWave / lpr);
-  const dim3 grid = grid_of((waves + 3) / 4), block(256);
+  geo.ntiles = (geo.nchunks + kDqFlatTile - 1) / kDqFlatTile;
+  geo.drow = (int32_t)(kWave / cpr);
+  geo.drem = (int32_t)(kWave % cpr);
+  const dim3 grid = grid_of((geo.ntiles + 3) / 4), block(256);
   const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
   switch (dt) {
-    case DT_F32: hipLaunchKernelGGL(k_nvfp4_dequant<DT_F32>, grid, block, 0, s, p, scales, row_scale, geo, y); break;
-    case DT_BF16: hipLaunchKernelGGL(k_nvfp4_dequant<DT_BF16>, grid, block, 0, s, p, scales, row_scale, geo, y); break;
-    default: hipLaunchKernelGGL(k_nvfp4_dequant<DT_F16>, grid, block, 0, s, p, scales, row_scale, geo, y); break;
+    case DT_F32: hipLaunchKernelGGL(k_nvfp4_dequant_flat<DT_F32>, grid, block, 0, s, p, scales, row_scale, geo, y); break;
+    case DT_BF16: hipLaunchKernelGGL(k_nvfp4_dequant_flat<DT_BF16>, grid, block, 0, s, p, scales, row_scale, geo, y); break;
+    default: hipLaunchKernelGGL(k_nvfp4_dequant_flat<DT_F16>, grid, block, 0, s, p, scales, row_scale, geo, y); break;
   }
   return hipGetLastError();
 }

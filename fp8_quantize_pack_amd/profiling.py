@@ -41,6 +41,12 @@ BENCH_KERNELS = {
     "cache_fp8": "mxq::k_cache_qdq<1, 0, 32>",
     "cache_mxfp4": "mxq::k_cache_qdq<1, 1, 32>",
     "cache_nvfp4": "mxq::k_cache_qdq<1, 2, 16>",
+    "mxfp8_quant": "mxq::k_mxfp8_quant<1>",
+    "mxfp8_dequant": "mxq::k_mxfp8_dequant<1>",
+    "fp4_static_qdq": "mxq::k_fp4_static_qdq<1>",
+    "kv_head_amax": "mxq::k_kv_head_amax<1, true, 16>",
+    "kv_quant": "mxq::k_kv_quant<1, true, 16>",
+    "kv_pages_dequant": "mxq::k_kv_pages_dequant<1>",
     "gemm_mxfp4_forward": "mxq::gmm::k_grouped_mm<1, 0, 128>",
     "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1, 128>",
     "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0, 128>",
@@ -50,8 +56,9 @@ CALIBRATION_MARK = "neg_kernel"
 
 
 # the sources of the kernels bench.py measures (names and contents hashed)
-CODEC_SOURCES = ("mxq_device.h", "mxq_kernel_common.h", "mxq_launch.h", "mxq_api.cpp",
-                 "k_mxfp4.hip", "k_nvfp4.hip", "k_cache.hip")
+CODEC_SOURCES = ("mxq_device.h", "mxq_kernel_common.h", "mxq_nvfp4_common.h", "mxq_launch.h",
+                 "mxq_api.cpp", "mxq_api_ext.cpp", "k_mxfp4.hip", "k_nvfp4.hip", "k_cache.hip",
+                 "k_mxfp8.hip", "k_fp4_static.hip", "k_kv.hip")
 
 
 def kernel_source_hash() -> str:
