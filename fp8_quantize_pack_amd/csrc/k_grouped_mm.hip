@@ -19,7 +19,9 @@
 // copied as is, the weight tile is dequantized in registers with the gfx950
 // fp4 converters on its way to LDS (transposed for the backward product).
 // The global loads of the next reduction step are issued before the MFMAs of
-// the current one.  Workgroups map to (expert, token tile, output tile) in an
+// the current one.  They are ordinary (temporal) loads: every activation
+// tile is read by all output-column tiles of its token tile and every weight
+// tile by all token tiles of its expert, and those reads meet in L2.  Workgroups map to (expert, token tile, output tile) in an
 // XCD-aware order (see xcd_logical); the per-expert tile counts come from offs
 // through a workgroup prefix sum, so
 // the host never reads offs.
@@ -93,14 +95,14 @@ __device__ __forceinline__ void load_stage(const Args& a, Stage<BM>& st, int tid
   for (int i = 0; i < BM / 32; ++i) {
     const int c = tid + THREADS * i;
     const int64_t row = m0 + (c >> 3);
-    st.av[i] = row < m1 ? stream_ld(reinterpret_cast<const u32x4*>(a.x + row * R + r0 + (c & 7) * 8))
+    st.av[i] = row < m1 ? *reinterpret_cast<const u32x4*>(a.x + row * R + r0 + (c & 7) * 8)
                         : u32x4{0u, 0u, 0u, 0u};
   }
   if constexpr (TRANS == 0) {
     // W_e rows c0 .. c0+127, columns r0 .. r0+63: thread -> (row tid/2, half tid%2)
     const int64_t row = e * a.N + c0 + (tid >> 1);
     const int64_t k = r0 + (tid & 1) * 32;
-    st.wv = stream_ld(reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2));
+    st.wv = *reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2);
     st.sb[0] = scale_at<FMT>(a, row, k);
     st.sb[1] = (FMT == FMT_MXFP4) ? st.sb[0] : scale_at<FMT>(a, row, k + 16);
     st.g[0] = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
@@ -109,7 +111,7 @@ __device__ __forceinline__ void load_stage(const Args& a, Stage<BM>& st, int tid
     // tid/4, quarter tid%4 of 32 columns); 4 lanes read each row's 64 bytes
     const int64_t row = e * a.N + r0 + (tid >> 2);
     const int64_t k = c0 + (tid & 3) * 32;
-    st.wv = stream_ld(reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2));
+    st.wv = *reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2);
     st.sb[0] = scale_at<FMT>(a, row, k);
     st.sb[1] = (FMT == FMT_MXFP4) ? st.sb[0] : scale_at<FMT>(a, row, k + 16);
     st.g[0] = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
