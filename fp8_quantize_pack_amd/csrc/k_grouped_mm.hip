@@ -14,10 +14,12 @@
 // Work: a workgroup (4 waves, 2 x 2) computes a BM x 128 output tile of one
 // expert (BM = 128 token rows) with v_mfma_f32_32x32x16_bf16 (each wave
 // BM/2 x 64 = BM/64 x 2 MFMA tiles), stepping the reduction by 64.
-// Both operands are staged in LDS as
-// [row][reduction] bf16 with 16-byte row padding; the activation tile is
-// copied as is, the weight tile is dequantized in registers with the gfx950
-// fp4 converters on its way to LDS (transposed for the backward product).
+// Both operands are staged in LDS.  The activation tile is copied as is,
+// [row][reduction] bf16 with 16-byte row padding.  The weight tile is
+// dequantized in registers with the gfx950 fp4 converters on its way to LDS:
+// for the forward product as [output column][reduction], for the backward as
+// the weights' own [reduction][output column] rows, read transposed into the
+// MFMA operand with ds_read_b64_tr_b16.
 // The global loads of the next reduction step are issued before the MFMAs of
 // the current one.  They are ordinary (temporal) loads: every activation
 // tile is read by all output-column tiles of its token tile and every weight
@@ -35,6 +37,10 @@ namespace gmm {
 constexpr int BN = 128;         // output columns per tile (token rows per tile: BM, 128 or 256)
 constexpr int BK = 64;          // reduction step
 constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (16-byte pad)
+// Backward weight tile: BK reduction rows of BN output columns, row-major,
+// with a 16-element pad (consecutive rows 8 banks apart).
+constexpr int WT_STRIDE = BN + 16;
+static_assert(BK * WT_STRIDE <= BN * LDS_STRIDE, "both weight-tile layouts share one LDS array");
 constexpr int THREADS = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -132,19 +138,35 @@ __device__ __forceinline__ void store_stage(const Stage<BM>& st, uint16_t* As, u
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<u32x4*>(dst + 8 * j) = deq8<FMT>(w[j], st.sb[j >> 1], st.g[0]);
   } else {
-    // transpose: weight (reduction row n, output column k) -> Bs[k][n]
+    // backward: weight row n (reduction), output columns kq .. kq+31 stay a
+    // row of the tile; the MFMA operand is transposed on the way out of LDS
     const int n = tid >> 2, kq = (tid & 3) * 32;
+    uint16_t* dst = Bs + n * WT_STRIDE + kq;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 d = deq8<FMT>(w[j], st.sb[j >> 1], st.g[0]);
-      const uint32_t v[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        Bs[(kq + 8 * j + 2 * h) * LDS_STRIDE + n] = (uint16_t)(v[h] & 0xFFFFu);
-        Bs[(kq + 8 * j + 2 * h + 1) * LDS_STRIDE + n] = (uint16_t)(v[h] >> 16);
-      }
-    }
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(dst + 8 * j) = deq8<FMT>(w[j], st.sb[j >> 1], st.g[0]);
   }
+}
+
+// Backward B operand of v_mfma_f32_32x32x16_bf16 from the row-major weight
+// tile: lane l needs reduction rows kk + 8 (l / 32) + 0..7 of output column
+// col0 + l % 32.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a
+// group receives, for t = 0..3, the 16-bit element at offset i % 4 of the 8
+// bytes that lane 4 t + i / 4 of the group addressed (checked on the chip).
+// So lane j of a group addresses row nb + j / 4, columns kc + 4 (j % 4) ..,
+// and lane i gets rows nb .. nb + 3 of column kc + i; two reads (nb, nb + 4)
+// give the 8 rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 read_b_trans(const uint16_t* Bs, int kk, int col0, int lane) {
+  const int g = lane >> 4, jl = lane & 15;
+  const int nb = kk + 8 * (g >> 1) + (jl >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (jl & 3);
+  typedef __attribute__((address_space(3))) s16x4* LdsS16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4)(Bs + nb * WT_STRIDE + col));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4)(Bs + (nb + 4) * WT_STRIDE + col));
+  const s16x4 v[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Which expert and token tile this workgroup owns: tile counts per expert,
@@ -243,9 +265,13 @@ __global__ __launch_bounds__(THREADS) void k_grouped_mm(Args a, int64_t ntiles_c
         af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                     As + (wm + 32 * i + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                    Bs + (wn + 32 * j + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)));
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (TRANS == 0)
+          bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                      Bs + (wn + 32 * j + (lane & 31)) * LDS_STRIDE + kk + 8 * (lane >> 5)));
+        else
+          bfr[j] = read_b_trans(Bs, kk, wn + 32 * j, lane);
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
