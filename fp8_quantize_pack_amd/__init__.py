@@ -405,11 +405,11 @@ def quantize_mxfp8(weight: torch.Tensor):
 def dequantize_mxfp8(codes: torch.Tensor, scales: torch.Tensor,
                      dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     """(e4m3 [..., K], e8m0 [..., K//32]) -> [..., K] in dtype."""
+    K = codes.shape[-1]
+    if K % MXFP8_BLOCK_SIZE or scales.shape[-1] != K // MXFP8_BLOCK_SIZE:
+        raise ValueError("codes/scales shapes do not describe 32-column blocks")
     c = _dev_input(codes.view(torch.uint8))
     s = _dev_input(scales.view(torch.uint8))
-    K = c.shape[-1]
-    if K % MXFP8_BLOCK_SIZE or s.shape[-1] != K // MXFP8_BLOCK_SIZE:
-        raise ValueError("codes/scales shapes do not describe 32-column blocks")
     y = torch.empty(*c.shape, dtype=dtype, device=c.device)
     mxq_dequantize_mxfp8(c, s, y)
     return y

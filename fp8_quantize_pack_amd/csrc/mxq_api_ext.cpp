@@ -5,16 +5,10 @@
 
 #include <stdint.h>
 
+#include "mxq_api_util.h"
 #include "mxq_launch.h"
 
-namespace {
-
-bool bad_dtype(mxq_dtype d) { return d != MXQ_F32 && d != MXQ_BF16 && d != MXQ_F16; }
-bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
-bool mul_overflows(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
-mxq_status launched(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_E_LAUNCH; }
-
-}  // namespace
+using namespace mxq::api;
 
 extern "C" {
 

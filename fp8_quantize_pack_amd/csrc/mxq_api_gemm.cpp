@@ -5,15 +5,15 @@
 
 #include <stdint.h>
 
+#include "mxq_api_util.h"
 #include "mxq_launch_gemm.h"
+
+using namespace mxq::api;
 
 namespace {
 
 constexpr int64_t kTile = 128;            // N and K are whole numbers of output / reduction tiles
 constexpr int64_t kMaxOutputTiles = 65535;
-
-bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
-bool mul_overflows(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
 
 mxq_status check(const void* x, mxq_dtype xdt, int64_t T, const void* packed,
                  const void* scales, int64_t E, int64_t N, int64_t K,
@@ -32,8 +32,6 @@ mxq_status check(const void* x, mxq_dtype xdt, int64_t T, const void* packed,
   if (misaligned(x) || misaligned(packed) || misaligned(y)) return MXQ_E_ALIGN;
   return MXQ_OK;
 }
-
-mxq_status launched(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_E_LAUNCH; }
 
 }  // namespace
 

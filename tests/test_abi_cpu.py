@@ -176,3 +176,28 @@ def test_python_wrapper_raises_page_errors_on_cpu_tensors():
         mxq.quantize_mxfp4(torch.zeros(2, 64))
     with pytest.raises(ValueError, match="cache format"):
         mxq.quantize_cache(torch.zeros(2, 64), "int4", 32)
+
+
+def test_python_wrappers_of_the_newer_calls_check_their_arguments():
+    import torch
+    import fp8_quantize_pack_amd as mxq
+    with pytest.raises(ValueError, match="divisible by 32"):
+        mxq.quantize_mxfp8(torch.zeros(2, 48))
+    with pytest.raises(ValueError, match="32-column blocks"):
+        mxq.dequantize_mxfp8(torch.zeros(2, 64, dtype=torch.uint8), torch.zeros(2, 3, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="power of two"):
+        mxq.fake_quantize_fp4_static(torch.zeros(2, 48), torch.zeros(2, 4), torch.ones(1), 12)
+    with pytest.raises(ValueError, match="whole number"):
+        mxq.fake_quantize_fp4_static(torch.zeros(2, 48), torch.zeros(2, 4), torch.ones(1), 32)
+    with pytest.raises(ValueError, match="power of two"):
+        mxq.quantize_kv_nvfp4(torch.zeros(4, 2, 96))
+    with pytest.raises(ValueError, match="tokens, heads, head_dim"):
+        mxq.quantize_kv_nvfp4(torch.zeros(4, 128))
+    with pytest.raises(ValueError, match="same blocks"):
+        mxq.dequantize_kv_cache([torch.zeros(4, 64, dtype=torch.uint8)], [], [], 2, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        mxq.dequantize_kv_cache([torch.zeros(4, 64, dtype=torch.uint8)],
+                                [torch.zeros(4, 8, dtype=torch.uint8)], [torch.ones(1)], 2, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        mxq.quantize_mxfp8(torch.zeros(2, 64))
+
