@@ -1,4 +1,5 @@
-"""The C-ABI calls under stream semantics and HIP graph capture.
+"""The C-ABI calls under stream semantics and HIP graph capture (the codec
+calls, MXFP8, the static FP4 round trip and both NVFP4 KV-cache calls).
 
 Every call only enqueues on the stream it is given, allocates nothing and
 clears its own scratch with a kernel (no memset nodes), so a captured
@@ -34,11 +35,36 @@ def _buffers():
         "nt_g": torch.empty(R, dtype=torch.float32, device=DEV),
         "scratch": torch.zeros(4, dtype=torch.float32, device=DEV),
         "kv_y": torch.empty_like(kv),
+        "m8_c": torch.empty(3, 256, K, dtype=torch.uint8, device=DEV),
+        "m8_s": torch.empty(3, 256, K // 32, dtype=torch.uint8, device=DEV),
+        "m8_y": torch.empty_like(x),
+        "st_y": torch.empty_like(x),
+        "kq_p": torch.empty(64, 8, 64, dtype=torch.uint8, device=DEV),
+        "kq_s": torch.empty(64, 8, 8, dtype=torch.uint8, device=DEV),
+        "kq_g": torch.empty(64, 8, dtype=torch.float32, device=DEV),
+        "kq_amax": torch.zeros(8 * 32, dtype=torch.float32, device=DEV),
+        "pg_y": torch.empty(64, 8, 128, dtype=torch.bfloat16, device=DEV),
     }
     return x, kv, out
 
 
-def _sequence(x, kv, o, stream=None):
+def _static_inputs(x):
+    a = x.float().abs().reshape(-1, 1024 // 16, 16).amax(-1).contiguous()
+    g = x.float().abs().max().reshape(1).contiguous()
+    return a, g
+
+
+def _kv_inputs():
+    k = synth.kv_cache((64, 8, 128), seed=93).to(DEV)
+    blocks = [(synth.kv_cache((16 * 8, 64), seed=94 + b).to(DEV).view(torch.uint8)[:, :64].contiguous(),
+               torch.randint(0x20, 0x50, (16 * 8, 8), dtype=torch.uint8,
+                             generator=torch.Generator().manual_seed(95 + b)).to(DEV),
+               torch.tensor([1.5 + b], dtype=torch.float32, device=DEV)) for b in range(4)]
+    tab = lambda i: torch.tensor([blk[i].data_ptr() for blk in blocks], dtype=torch.int64).to(DEV)
+    return k, blocks, (tab(0), tab(1), tab(2))
+
+
+def _sequence(x, kv, o, stream=None, extra=None):
     m = mxq()
     m.mxq_quantize_mxfp4(x, o["mx_p"], o["mx_s"], stream)
     m.mxq_dequantize_mxfp4(o["mx_p"], o["mx_s"], o["mx_y"], stream)
@@ -46,10 +72,17 @@ def _sequence(x, kv, o, stream=None):
     m.mxq_quantize_nvfp4(x, o["nt_p"], o["nt_s"], o["nt_g"], mode="tensor", scratch=o["scratch"],
                          stream=stream)
     m.mxq_quantize_cache(kv, o["kv_y"], "nvfp4", 16, stream)
+    if extra is not None:
+        (a, g), (k, _, (vt, st, at)) = extra
+        m.mxq_quantize_mxfp8(x, o["m8_c"], o["m8_s"], stream)
+        m.mxq_dequantize_mxfp8(o["m8_c"], o["m8_s"], o["m8_y"], stream)
+        m.mxq_fake_quantize_fp4_static(x, a, g, o["st_y"], 16, stream)
+        m.mxq_quantize_kv_nvfp4(k, o["kq_amax"], o["kq_p"], o["kq_s"], o["kq_g"], True, stream)
+        m.mxq_dequantize_kv_pages_nvfp4(vt, st, at, 16, o["pg_y"], stream)
 
 
 def _snapshot(o):
-    return {k: v.clone() for k, v in o.items() if k != "scratch"}
+    return {k: v.clone() for k, v in o.items() if k not in ("scratch", "kq_amax")}
 
 
 def _same(a, b):
@@ -59,7 +92,8 @@ def _same(a, b):
 
 def test_graph_capture_replays_match_eager():
     x, kv, o = _buffers()
-    _sequence(x, kv, o)
+    extra = (_static_inputs(x), _kv_inputs())
+    _sequence(x, kv, o, extra=extra)
     torch.cuda.synchronize()
     eager = _snapshot(o)
     for v in o.values():
@@ -67,12 +101,13 @@ def test_graph_capture_replays_match_eager():
     s = torch.cuda.Stream()                       # default priority
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        _sequence(x, kv, o, s)
+        _sequence(x, kv, o, s, extra=extra)
     for replay in range(3):
         for k, v in o.items():
-            if k != "scratch":
+            if k not in ("scratch", "kq_amax"):
                 v.fill_(0x5A if v.dtype == torch.uint8 else 7)   # poison the outputs
         o["scratch"].fill_(123.0)                 # stale scratch: the graph must clear it
+        o["kq_amax"].fill_(1e30)
         torch.randn(1 << 20, device=DEV).sum()    # unrelated eager work between replays
         torch.cuda.synchronize()
         g.replay()
@@ -84,7 +119,8 @@ def test_side_stream_orders_after_producer():
     """A call on a side stream that waits on the producer's event sees the
     producer's data; results equal the default-stream results."""
     x, kv, o = _buffers()
-    _sequence(x, kv, o)
+    extra = (_static_inputs(x), _kv_inputs())
+    _sequence(x, kv, o, extra=extra)
     torch.cuda.synchronize()
     ref = _snapshot(o)
     s = torch.cuda.Stream()
@@ -96,6 +132,6 @@ def test_side_stream_orders_after_producer():
     with torch.cuda.stream(s):
         for v in o.values():
             v.zero_()
-        _sequence(x2, kv, o, s)
+        _sequence(x2, kv, o, s, extra=extra)
     s.synchronize()
     _same(ref, _snapshot(o))
