@@ -290,9 +290,10 @@ def extra_ops(torch, mxq, synth, dev, x, y, reps):
     `reps` launches on resident inputs, with its algorithmic bytes (inputs
     read once, outputs written once) and its fraction of the HBM peak; not
     part of `value`.
-      * MXFP8 quantize / dequantize and the static two-level FP4 round trip
-        (block 16, calibrated block amax) on one 36-expert chunk of the sweep,
-        bf16 [36, 2048, 7168];
+      * MXFP8 quantize / dequantize, the static two-level FP4 round trip
+        (block 16, calibrated block amax) and per-tensor NVFP4 quantize (a
+        whole-tensor amax pass, then the quantize pass) on one 36-expert
+        chunk of the sweep, bf16 [36, 2048, 7168];
       * the NVFP4 KV cache: per-head quantization with k_smooth of K
         [32768, 12, 128] bf16 (two kernels: the per-head amax pass and the
         quantize pass; its bytes count K read once), and the paged
@@ -324,6 +325,18 @@ def extra_ops(torch, mxq, synth, dev, x, y, reps):
            _time_launches(torch, lambda: mxq.mxq_fake_quantize_fp4_static(xs, amax, gam, ys, 16), reps),
            shape=list(xs.shape), block=16)
     del amax
+    # per-tensor NVFP4 (one amax for the whole tensor: a read pass, then the
+    # quantize pass); bytes count the input once
+    rows = ne * xs.shape[1]
+    tp = torch.empty((*xs.shape[:-1], K // 2), dtype=torch.uint8, device=dev)
+    ts = torch.empty((*xs.shape[:-1], K // 16), dtype=torch.uint8, device=dev)
+    tg = torch.empty(xs.shape[:-1], dtype=torch.float32, device=dev)
+    scr = torch.zeros(1, dtype=torch.float32, device=dev)
+    record("nvfp4_quant_tensor_mode", bytes_nv(n, rows),
+           _time_launches(torch, lambda: mxq.mxq_quantize_nvfp4(xs, tp, ts, tg, mode="tensor",
+                                                               scratch=scr), reps),
+           shape=list(xs.shape))
+    del tp, ts, tg
     S, H, D, bt = 32768, 12, 128, 1024
     k = synth.kv_cache((S, H, D), seed=5, device=dev)
     kp = torch.empty((S, H, D // 2), dtype=torch.uint8, device=dev)

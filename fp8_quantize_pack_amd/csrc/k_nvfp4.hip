@@ -220,7 +220,14 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_short(
 // chunks, reduced per wave and combined with an integer atomic max on the bit
 // patterns (non-negative floats order like their patterns).
 // Whole-tensor amax: a grid-stride pass with four chunks in flight per lane
-// (magnitude maxima on the raw 16-bit patterns), one atomic maximum per wave.
+// (magnitude maxima on the raw 16-bit patterns); the waves of a workgroup
+// combine through LDS and issue one atomic maximum (atomics on one address
+// serialize, so their number is kept to the workgroup count).
+#ifndef MXQ_TENSOR_AMAX_BLOCKS
+#define MXQ_TENSOR_AMAX_BLOCKS 4096
+#endif
+constexpr int64_t kTensorAmaxBlocks = MXQ_TENSOR_AMAX_BLOCKS;
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_tensor_amax(const void* __restrict__ x,
                                                      int64_t nchunks,
@@ -236,8 +243,14 @@ __global__ __launch_bounds__(256) void k_tensor_amax(const void* __restrict__ x,
     for (int u = 0; u < 4; ++u) m = max(m, amax8_bits<DT>(r[u]));
   }
   for (; c < nchunks; c += stride) m = max(m, amax8_bits<DT>(ld8<DT>(x, c)));
+  __shared__ uint32_t s_wave[4];
   const float amax = group_max<64>(amax_from_bits<DT>(m));
-  if ((threadIdx.x & 63) == 0) atomicMax(out, fbits(amax));
+  if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = fbits(amax);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t w = max(max(s_wave[0], s_wave[1]), max(s_wave[2], s_wave[3]));
+    atomicMax(out, w);
+  }
 }
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
@@ -408,7 +421,7 @@ hipError_t launch_nvfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
   if (mode == 2) {
     const int64_t nchunks = rows * (K / 8);
     int64_t b = (nchunks + 255) / 256;
-    const int gb = (int)(b < 1024 ? b : 1024);
+    const int gb = (int)(b < kTensorAmaxBlocks ? b : kTensorAmaxBlocks);
     hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, ta, 0u);
     switch (dt) {
       case DT_F32: hipLaunchKernelGGL(k_tensor_amax<DT_F32>, dim3(gb), dim3(256), 0, s, x, nchunks, ta); break;

@@ -41,6 +41,7 @@ BENCH_KERNELS = {
     "cache_fp8": "mxq::k_cache_qdq<1, 0, 32>",
     "cache_mxfp4": "mxq::k_cache_qdq<1, 1, 32>",
     "cache_nvfp4": "mxq::k_cache_qdq<1, 2, 16>",
+    "nvfp4_tensor_amax": "mxq::k_tensor_amax<1>",
     "mxfp8_quant": "mxq::k_mxfp8_quant<1>",
     "mxfp8_dequant": "mxq::k_mxfp8_dequant<1>",
     "fp4_static_qdq": "mxq::k_fp4_static_qdq<1>",
