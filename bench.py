@@ -326,16 +326,21 @@ def extra_ops(torch, mxq, synth, dev, x, y, reps):
            shape=list(xs.shape), block=16)
     del amax
     # per-tensor NVFP4 (one amax for the whole tensor: a read pass, then the
-    # quantize pass); bytes count the input once
-    rows = ne * xs.shape[1]
-    tp = torch.empty((*xs.shape[:-1], K // 2), dtype=torch.uint8, device=dev)
-    ts = torch.empty((*xs.shape[:-1], K // 16), dtype=torch.uint8, device=dev)
-    tg = torch.empty(xs.shape[:-1], dtype=torch.float32, device=dev)
+    # quantize pass); bytes count the input once.  One scale for the whole
+    # tensor makes the row length irrelevant to the result (16-value blocks
+    # are the same), so the chunk is viewed as rows of 4096: the row kernel
+    # instantiation differs from the sweep's, which keeps the two apart in
+    # per-kernel profiles.
+    xt = xs.reshape(-1, 4096)
+    rows = xt.shape[0]
+    tp = torch.empty((rows, 4096 // 2), dtype=torch.uint8, device=dev)
+    ts = torch.empty((rows, 4096 // 16), dtype=torch.uint8, device=dev)
+    tg = torch.empty(rows, dtype=torch.float32, device=dev)
     scr = torch.zeros(1, dtype=torch.float32, device=dev)
     record("nvfp4_quant_tensor_mode", bytes_nv(n, rows),
-           _time_launches(torch, lambda: mxq.mxq_quantize_nvfp4(xs, tp, ts, tg, mode="tensor",
+           _time_launches(torch, lambda: mxq.mxq_quantize_nvfp4(xt, tp, ts, tg, mode="tensor",
                                                                scratch=scr), reps),
-           shape=list(xs.shape))
+           shape=[rows, 4096])
     del tp, ts, tg
     S, H, D, bt = 32768, 12, 128, 1024
     k = synth.kv_cache((S, H, D), seed=5, device=dev)

@@ -42,6 +42,7 @@ BENCH_KERNELS = {
     "cache_mxfp4": "mxq::k_cache_qdq<1, 1, 32>",
     "cache_nvfp4": "mxq::k_cache_qdq<1, 2, 16>",
     "nvfp4_tensor_amax": "mxq::k_tensor_amax<1>",
+    "nvfp4_quant_tensor_mode": "mxq::k_nvfp4_quant_seg<1, 4, 1, true>",
     "mxfp8_quant": "mxq::k_mxfp8_quant<1>",
     "mxfp8_dequant": "mxq::k_mxfp8_dequant<1>",
     "fp4_static_qdq": "mxq::k_fp4_static_qdq<1>",
