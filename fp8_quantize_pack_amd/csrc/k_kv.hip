@@ -20,18 +20,19 @@
 //
 // Quantization with k_smooth.  k [S, H, D], D a power of two in [16, 512].
 // Each row (token, head) of D values is optionally smoothed: its mean is the
-// binary32 pairwise sum (16 values in a lane, then a butterfly over the D / 16
+// binary32 pairwise sum (8 values in a lane, then a butterfly over the D / 8
 // lanes of the row: the pairwise tree, since every addition is commutative)
 // times 1 / D, rounded to the dtype; each value minus that mean is evaluated
 // in binary32 and rounded to the dtype.  Every head's slice then gets one
 // global scale g = amax(slice) / 2688 and the NVFP4 codes of the nvfp4 page.
-// Pass 1 reduces the per-head maxima of the (smoothed) values: each
-// workgroup owns a contiguous range of rows, folds them into per-head maxima
-// in LDS, then issues one global atomic maximum per head; pass 2 recomputes
-// the smoothed values (deterministic) and quantizes, one binary64 block
-// reciprocal per lane and 16 values (lane pairs share blocks, as in the
-// NVFP4 row kernel).  Every load and store instruction of a wave covers one
-// contiguous range.
+// Both passes run on a fixed grid whose waves stride over tiles of 128
+// chunks (lane l holds chunks l and 64 + l).  Pass 1 folds the per-head
+// maxima of the (smoothed) values in LDS and adds one atomic maximum per head
+// and workgroup into one of 32 slots per head; pass 2 reduces the slots into
+// per-head g and 1 / g tables in LDS, recomputes the smoothed values
+// (deterministic) and quantizes, one binary64 block reciprocal per lane pair
+// and 16 values (as in the NVFP4 row kernel).  Every load and store
+// instruction of a wave covers one contiguous range.
 #include "mxq_kernel_common.h"
 #include "mxq_launch.h"
 #include "mxq_nvfp4_common.h"

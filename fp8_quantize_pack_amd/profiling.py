@@ -65,14 +65,39 @@ CODEC_SOURCES = ("mxq_device.h", "mxq_kernel_common.h", "mxq_nvfp4_common.h",
                  "k_mxfp8.hip", "k_fp4_static.hip", "k_kv.hip")
 
 
+def code_tokens(text: str) -> str:
+    """C/C++/HIP source with comments removed and runs of whitespace folded:
+    what the compiler sees, so comment-only edits keep a measurement valid."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":                       # string / char literal, kept verbatim
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the codec kernel sources under csrc/."""
+    """Hash of the codec kernel sources under csrc/ (code only, see code_tokens)."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
     for f in CODEC_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode())
-            h.update(fh.read())
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -48,3 +48,12 @@ def test_trace_table_maps_bench_ops_to_kernels(tmp_path):
     row = [l for l in txt.splitlines() if l.startswith("mxfp4_quant")][0].split()
     assert row[1] == "mxq::k_mxfp4_quant<1>" and row[2] == "8" and row[3] == "200.00"
     assert "some_other_kernel" in txt
+
+
+def test_code_tokens_ignore_comments_and_layout_only():
+    a = "int x = 1; // one\n/* block\n comment */ float y;\nconst char* s = \"// not a comment\";"
+    b = "int x = 1;\n\n   float y;   const char* s = \"// not a comment\";"
+    assert prof.code_tokens(a) == prof.code_tokens(b)
+    assert prof.code_tokens("int x = 1;") != prof.code_tokens("int x = 2;")
+    assert "// not a comment" in prof.code_tokens(a)
+
