@@ -163,7 +163,10 @@ __device__ __forceinline__ void k_smooth8(float f[8]) {
 // D values is L = D / 8 consecutive chunks and never straddles the two
 // halves (L divides 64); the 16-value blocks are lane pairs.  The grid is a
 // fixed number of workgroups whose waves stride over the tiles, so that each
-// workgroup's set-up (LDS tables, the final atomics) is paid once.
+// workgroup's set-up (LDS tables, the final atomics) is paid once.  The host
+// makes the stride (in rows) a multiple of the head count, so the heads of a
+// lane's two rows are the same in every tile it visits: a lane keeps its
+// running maxima (pass 1) and its heads' scales (pass 2) in registers.
 #ifndef MXQ_KV_GRID_BLOCKS
 #define MXQ_KV_GRID_BLOCKS 1024
 #endif
@@ -181,16 +184,17 @@ struct KvGeom {
 
 // Each head's maximum is spread over kKvAmaxSlots words (workgroup b folds
 // into slot b % kKvAmaxSlots), which keeps the atomics on one address few.
-constexpr int kKvAmaxSlots = 32;
+#ifndef MXQ_KV_AMAX_SLOTS
+#define MXQ_KV_AMAX_SLOTS 32
+#endif
+constexpr int kKvAmaxSlots = MXQ_KV_AMAX_SLOTS;
 
-// Tile, rows and heads of this lane's two chunks, advanced by the wave stride.
+// First tile, tile stride, first row of this lane's chunk l, and the heads of
+// its two rows (row_a and row_a + 64 / L), which the stride leaves unchanged.
 template <int L>
 struct KvRows {
-  int64_t tile;       // current tile of this wave
-  int64_t stride;     // waves in the grid
-  int64_t row_a;      // row of chunk l; the row of chunk 64 + l is row_a + 64 / L
+  int64_t tile, stride, row_a;
   uint32_t h_a, h_b;
-  uint32_t step;      // head advance per stride
   __device__ __forceinline__ KvRows(const KvGeom& geo) {
     constexpr int R = 128 / L;                           // rows per tile
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -199,13 +203,6 @@ struct KvRows {
     row_a = tile * R + lane / L;
     h_a = (uint32_t)(row_a % geo.H);
     h_b = (uint32_t)((row_a + R / 2) % geo.H);
-    step = (uint32_t)((stride * R) % geo.H);
-  }
-  __device__ __forceinline__ void advance(int H) {
-    tile += stride;
-    row_a += stride * (128 / L);
-    h_a += step; h_a = h_a >= (uint32_t)H ? h_a - H : h_a;
-    h_b += step; h_b = h_b >= (uint32_t)H ? h_b - H : h_b;
   }
 };
 
@@ -228,15 +225,15 @@ __global__ __launch_bounds__(256) void k_kv_head_amax(const void* __restrict__ k
   constexpr int U = kKvRowUnroll;
   for (int i = threadIdx.x; i < geo.H; i += blockDim.x) s_max[i] = 0u;
   __syncthreads();
-  const bool first = (threadIdx.x & (L - 1)) == 0;      // first lane of its row
-  KvRows<L> rr(geo);
-  while (rr.tile < geo.tiles) {                          // uniform over the wave
+  const KvRows<L> rr(geo);
+  float m0 = 0.0f, m1 = 0.0f;           // running maxima of the lane's two rows' heads
+  // chunks past the end load as zeros, which leave a maximum unchanged
+  for (int64_t tile = rr.tile; tile < geo.tiles; tile += U * rr.stride) {   // uniform
     KvTile<DT> t[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT>(k, geo, rr.tile + u * rr.stride);
+    for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT>(k, geo, tile + u * rr.stride);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t c = rr.tile * 128 + (threadIdx.x & 63);
       float f0[8], f1[8];
       unpack8<DT>(t[u].c0, f0);
       unpack8<DT>(t[u].c1, f1);
@@ -244,18 +241,18 @@ __global__ __launch_bounds__(256) void k_kv_head_amax(const void* __restrict__ k
         k_smooth8<DT, L>(f0);
         k_smooth8<DT, L>(f1);
       }
-      float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        a0 = fmaxf(a0, fabsf(f0[i]));
-        a1 = fmaxf(a1, fabsf(f1[i]));
+        m0 = fmaxf(m0, fabsf(f0[i]));
+        m1 = fmaxf(m1, fabsf(f1[i]));
       }
-      a0 = group_max<L>(a0);
-      a1 = group_max<L>(a1);
-      if (first && c < geo.nchunks) atomicMax(&s_max[rr.h_a], fbits(a0));
-      if (first && c + 64 < geo.nchunks) atomicMax(&s_max[rr.h_b], fbits(a1));
-      rr.advance(geo.H);
     }
+  }
+  m0 = group_max<L>(m0);
+  m1 = group_max<L>(m1);
+  if ((threadIdx.x & (L - 1)) == 0) {                   // first lane of its row
+    atomicMax(&s_max[rr.h_a], fbits(m0));
+    atomicMax(&s_max[rr.h_b], fbits(m1));
   }
   __syncthreads();
   const int slot = blockIdx.x % kKvAmaxSlots;
@@ -284,17 +281,24 @@ __global__ __launch_bounds__(256) void k_kv_quant(const void* __restrict__ k, Kv
   }
   __syncthreads();
   constexpr int U = kKvRowUnroll;
+  constexpr int R = 128 / L;
   const int lane = threadIdx.x & 63;
   const bool odd = lane & 1;
   const bool first = (lane & (L - 1)) == 0;
-  KvRows<L> rr(geo);
-  while (rr.tile < geo.tiles) {                          // uniform over the wave
+  const KvRows<L> rr(geo);
+  // the even lane of a pair scales chunk 0's block (row a), the odd lane
+  // chunk 1's block (row b)
+  const float g_a = s_g[rr.h_a], g_b = s_g[rr.h_b];
+  const float g_m = odd ? g_b : g_a;
+  const double rg_m = s_rg[odd ? rr.h_b : rr.h_a];
+  for (int64_t tile = rr.tile; tile < geo.tiles; tile += U * rr.stride) {   // uniform
     KvTile<DT> t[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT>(k, geo, rr.tile + u * rr.stride);
+    for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT>(k, geo, tile + u * rr.stride);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t c = rr.tile * 128 + lane;
+      const int64_t tu = tile + u * rr.stride;
+      const int64_t c = tu * 128 + lane;
       float f0[8], f1[8];
       unpack8<DT>(t[u].c0, f0);
       unpack8<DT>(t[u].c1, f1);
@@ -302,8 +306,7 @@ __global__ __launch_bounds__(256) void k_kv_quant(const void* __restrict__ k, Kv
         k_smooth8<DT, L>(f0);
         k_smooth8<DT, L>(f1);
       }
-      // block maxima of both chunks (the block is this lane pair); the even
-      // lane takes the scale of chunk 0's block, the odd lane that of chunk 1's
+      // block maxima of both chunks (the block is this lane pair)
       float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -312,9 +315,8 @@ __global__ __launch_bounds__(256) void k_kv_quant(const void* __restrict__ k, Kv
       }
       a0 = bitsf(max(fbits(a0), pair_swap(fbits(a0))));
       a1 = bitsf(max(fbits(a1), pair_swap(fbits(a1))));
-      const uint32_t hm = odd ? rr.h_b : rr.h_a;
       uint32_t sb;
-      const double mine = nv_block_recip(odd ? a1 : a0, s_g[hm], s_rg[hm], sb);
+      const double mine = nv_block_recip(odd ? a1 : a0, g_m, rg_m, sb);
       const double other = pair_swap(mine);
       const double r0 = odd ? other : mine, r1 = odd ? mine : other;
       float q[8];
@@ -328,9 +330,9 @@ __global__ __launch_bounds__(256) void k_kv_quant(const void* __restrict__ k, Kv
       if (c < geo.nchunks) stream_st(w0, packed + c);
       if (c + 64 < geo.nchunks) stream_st(w1, packed + c + 64);
       if (cm < geo.nchunks) scales[cm >> 1] = (uint8_t)sb;
-      if (first && c < geo.nchunks) row_scale[rr.row_a] = s_g[rr.h_a];
-      if (first && c + 64 < geo.nchunks) row_scale[rr.row_a + 64 / L] = s_g[rr.h_b];
-      rr.advance(geo.H);
+      const int64_t row = tu * R + lane / L;
+      if (first && c < geo.nchunks) row_scale[row] = g_a;
+      if (first && c + 64 < geo.nchunks) row_scale[row + R / 2] = g_b;
     }
   }
 }
@@ -380,8 +382,16 @@ hipError_t launch_kv_quant(const void* k, int dt, int64_t S, int64_t H, int64_t 
   geo.nchunks = S * H * (D / 8);
   geo.tiles = (geo.nchunks + 127) / 128;
   geo.H = (int)H;
+  // workgroups: about kKvGridBlocks (fewer for small tensors), a multiple of
+  // q = H / gcd(4 * rows per tile, H), so that the stride of the grid's
+  // 4 * nblk waves, 4 * nblk * rows per tile rows, is a multiple of H
+  const int64_t rows_per_tile = 1024 / D;
+  int64_t a = 4 * rows_per_tile, b = H;
+  while (b != 0) { const int64_t r = a % b; a = b; b = r; }
+  const int64_t q = H / a;
   int64_t nblk = (geo.tiles + 3) / 4;
   nblk = nblk < kKvGridBlocks ? nblk : kKvGridBlocks;
+  nblk = (nblk + q - 1) / q * q;
   uint32_t* ha = reinterpret_cast<uint32_t*>(head_amax);
   const int nslots = (int)H * kKvAmaxSlots;
   hipLaunchKernelGGL(k_fill_head_amax, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, ha, nslots);

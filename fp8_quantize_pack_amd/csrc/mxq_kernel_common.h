@@ -171,9 +171,10 @@ constexpr uint32_t kSrHalfDownOdd = 0x3FFFFF00u;    // element 1 of a pair
 __device__ __forceinline__ float e8m0_as_scale(uint32_t b) { return bitsf(b << 23); }
 
 // One pair through the stochastic-rounding quantizer, result in byte 0.
-// (The builtin's "old" operand is not tied to its result by the compiler, so
-// the byte-select forms cannot be chained; every pair is converted into byte
-// 0 of a fresh value and the bytes are assembled with v_perm_b32.)
+// (This builtin's "old" operand is not tied to its result by the compiler, so
+// its byte-select forms cannot be chained; every pair is converted into byte
+// 0 of a fresh value and the bytes are assembled with v_perm_b32.  The
+// round-to-nearest-even form below is tied and is chained.)
 __device__ __forceinline__ uint32_t sr_fp4_pair(float a, float b, uint32_t seed, float scale) {
   return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{a, b}, seed, scale, 0);
 }
@@ -213,13 +214,13 @@ __device__ __forceinline__ uint32_t e2m1_pack8_hw(const float f[8], float scale)
 // even (checked on all |value / scale| < 8 for several scales).
 constexpr float kTieDown = 0x1.fffffep-1f;
 
-__device__ __forceinline__ uint32_t rne_fp4_pair(float a, float b, float scale) {
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a * kTieDown, b * kTieDown, scale, 0);
-}
-
+// Pair k of the 8 values goes to byte k of one register: the converter's
+// byte select writes that byte and keeps the others.
 __device__ __forceinline__ uint32_t e2m1_pack8_rne(const float f[8], float scale) {
-  return gather_byte0(rne_fp4_pair(f[0], f[1], scale), rne_fp4_pair(f[2], f[3], scale),
-                      rne_fp4_pair(f[4], f[5], scale), rne_fp4_pair(f[6], f[7], scale));
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0] * kTieDown, f[1] * kTieDown, scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2] * kTieDown, f[3] * kTieDown, scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4] * kTieDown, f[5] * kTieDown, scale, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6] * kTieDown, f[7] * kTieDown, scale, 3);
 }
 
 // Clear the sign bit of every zero-magnitude nibble (code 8 -> 0), so that it

@@ -155,3 +155,47 @@ def test_grouped_mm_nvfp4_c3_expert_shape(transpose):
     rows = sorted({r for a, b in zip([0] + ends[:-1], ends) if b > a for r in (a, b - 1, (a + b) // 2)})
     ref, absref = oracle.grouped_mm(x, wd, offs, transpose, rows=rows)
     _check(y[rows], ref, absref, N if transpose else K, "nvfp4 C3")
+
+
+# ------------------------------------------------------------------ the fused dequantization, bit for bit
+
+def _byte_weights(fmt, E, N, K, seed):
+    """Every code in every position under scale bytes spread over their range
+    (finite, no overflow or bfloat16 subnormals, so that the one-hot products
+    below are exact): random code bytes, MXFP4 e8m0 bytes in [27, 227], NVFP4
+    e4m3 bytes of both signs and both zeros (no NaN bytes), row scales of a
+    quantized tensor."""
+    rng = np.random.default_rng(seed)
+    p = torch.from_numpy(rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8))
+    if fmt == "mxfp4":
+        s = torch.from_numpy(rng.integers(27, 228, (E, N, K // 32), dtype=np.uint8))
+        return (p, s), oracle.dequantize_mxfp4(p, s, torch.bfloat16)
+    sb = rng.integers(0, 256, (E, N, K // 16), dtype=np.uint8)
+    sb[(sb & 0x7F) == 0x7F] = 0x7E                     # no NaN scales
+    sb.reshape(-1)[:4] = [0x00, 0x80, 0x01, 0x81]       # both zeros, smallest subnormals
+    s = torch.from_numpy(sb)
+    _, _, g = oracle.quantize_nvfp4(synth.moe_nvfp4((E, N, K), seed=seed))
+    return (p, s, g), oracle.dequantize_nvfp4(p, s, g, torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_grouped_mm_one_hot_reproduces_dequantized_weights(fmt, transpose):
+    """With one-hot activation rows every output is one weight times 1.0 plus
+    zeros, so the GEMM must return the dequantized weights exactly: W_e^T in
+    the forward (rows over k), W_e in the backward (rows over n).  This pins
+    the in-register dequantization to the dequantize definition bit for bit
+    (zeros compared as values: their sign follows the accumulation)."""
+    E, N, K = 2, 128, 256
+    q, wd = _byte_weights(fmt, E, N, K, seed=38)
+    R = N if transpose else K
+    x = torch.eye(R, dtype=torch.bfloat16).repeat(E, 1)
+    offs = _offs([R] * E)
+    y = _run(fmt, q, x, offs, transpose,
+             torch.empty(E * R, K if transpose else N, dtype=torch.bfloat16, device=DEV))
+    ref = torch.cat([wd[e] if transpose else wd[e].t() for e in range(E)]).contiguous()
+    zero = ref.float() == 0
+    assert torch.equal(y.float() == 0, zero), "zero pattern differs"
+    yb, rb = y.view(torch.int16), ref.view(torch.int16)
+    bad = (yb != rb) & ~zero
+    assert not bad.any(), f"{fmt}: {int(bad.sum())} weights differ, first at {bad.nonzero()[:4].tolist()}"

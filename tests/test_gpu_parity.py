@@ -389,6 +389,30 @@ def test_nvfp4_dequant_every_code_every_scale(dtype):
     assert_same(y[~nan], yo[~nan], "dequant")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("K", [4096, 256])
+def test_nvfp4_dequant_all_codes_under_all_scale_bytes(K, dtype):
+    """Each of the 256 scale bytes (both zeros, negatives, NaN) over a block
+    holding the 16 codes 0..15, under row scales from zero and subnormal to
+    huge; rows of 4096 (segment kernel) and of 256 (short-row kernel)."""
+    say("nvfp4 dequant codes x scale bytes", K, dtype)
+    rng = np.random.default_rng(9)
+    R = 48
+    blk = torch.tensor([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], dtype=torch.uint8)
+    p = blk.repeat(R, 256)                                   # [R, 2048]: 256 blocks of codes 0..15
+    s = torch.arange(256, dtype=torch.uint8).repeat(R, 1)   # block j has scale byte j
+    g = torch.from_numpy(np.concatenate([np.exp2(rng.random(R - 8) * 60 - 40) * rng.choice([-1, 1], R - 8),
+                                         [0.0, -0.0, 1e-40, 3e38, 2.0 ** -126, 1.0, -6e4, float("inf")]])
+                         .astype(np.float32))
+    per = 4096 // K
+    p, s, g = p.reshape(R * per, K // 2), s.reshape(R * per, K // 16), g.repeat_interleave(per)
+    yo = oracle.dequantize_nvfp4(p, s, g, dtype)
+    y = gpu_dequantize_nvfp4(p.to(DEV), s.to(DEV), g.to(DEV), dtype).cpu()
+    nan = torch.isnan(yo.float())
+    assert torch.equal(nan, torch.isnan(y.float()))
+    assert_same(y[~nan], yo[~nan], "dequant")
+
+
 # ------------------------------------------------------------------ cache
 
 CACHE_CASES = [(512, 32), (128, 32), (512, 16), (120, 32), (100, 16), (96, 7), (64, 64),
