@@ -227,20 +227,25 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_short(
 #define MXQ_TENSOR_AMAX_BLOCKS 4096
 #endif
 constexpr int64_t kTensorAmaxBlocks = MXQ_TENSOR_AMAX_BLOCKS;
+#ifndef MXQ_TENSOR_AMAX_UNROLL
+#define MXQ_TENSOR_AMAX_UNROLL 4
+#endif
+constexpr int kTensorAmaxUnroll = MXQ_TENSOR_AMAX_UNROLL;   // loads in flight per thread
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_tensor_amax(const void* __restrict__ x,
                                                      int64_t nchunks,
                                                      uint32_t* __restrict__ out) {
+  constexpr int U = kTensorAmaxUnroll;
   uint32_t m = 0u;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; c + 3 * stride < nchunks; c += 4 * stride) {
-    Raw8<DT> r[4];
+  for (; c + (U - 1) * stride < nchunks; c += U * stride) {
+    Raw8<DT> r[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] = ld8<DT>(x, c + u * stride);
+    for (int u = 0; u < U; ++u) r[u] = ld8<DT>(x, c + u * stride);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) m = max(m, amax8_bits<DT>(r[u]));
+    for (int u = 0; u < U; ++u) m = max(m, amax8_bits<DT>(r[u]));
   }
   for (; c < nchunks; c += stride) m = max(m, amax8_bits<DT>(ld8<DT>(x, c)));
   __shared__ uint32_t s_wave[4];
