@@ -371,7 +371,7 @@ def extra_ops(torch, mxq, synth, dev, x, y, reps):
     nb = S // bt
     for c in sets:
         blocks = [(c["p"].reshape(nb, bt * H, D // 2)[b].clone(), c["s"].reshape(nb, bt * H, D // 16)[b].clone(),
-                   c["ha"][::mxq.KV_AMAX_SLOTS].max().reshape(1).clone()) for b in range(nb)]
+                   c["ha"][:H].max().reshape(1).clone()) for b in range(nb)]
         tab = lambda i: torch.tensor([blk[i].data_ptr() for blk in blocks], dtype=torch.int64).to(dev)
         c.update(blocks=blocks, vt=tab(0), st=tab(1), at=tab(2))
         del c["k"], c["p"], c["s"], c["g"]

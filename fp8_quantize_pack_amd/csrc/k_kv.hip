@@ -26,13 +26,14 @@
 // in binary32 and rounded to the dtype.  Every head's slice then gets one
 // global scale g = amax(slice) / 2688 and the NVFP4 codes of the nvfp4 page.
 // Both passes run on a fixed grid whose waves stride over tiles of 128
-// chunks (lane l holds chunks l and 64 + l).  Pass 1 folds the per-head
-// maxima of the (smoothed) values in LDS and adds one atomic maximum per head
-// and workgroup into one of 32 slots per head; pass 2 reduces the slots into
-// per-head g and 1 / g tables in LDS, recomputes the smoothed values
-// (deterministic) and quantizes, one binary64 block reciprocal per lane pair
-// and 16 values (as in the NVFP4 row kernel).  Every load and store
-// instruction of a wave covers one contiguous range.
+// chunks (lane l holds chunks l and 64 + l), loading the next step's tiles
+// before the current step's arithmetic.  Pass 1 keeps the maxima of the
+// (smoothed) values of its lane's two heads in registers, folds them in LDS
+// and adds one atomic maximum per head and workgroup into one of 32 slots per
+// head; pass 2 reduces the slots into per-head g and 1 / g tables in LDS,
+// recomputes the smoothed values (deterministic) and quantizes, one binary64
+// block reciprocal per lane pair and 16 values (as in the NVFP4 row kernel).
+// Every load and store instruction of a wave covers one contiguous range.
 #include "mxq_kernel_common.h"
 #include "mxq_launch.h"
 #include "mxq_nvfp4_common.h"
@@ -167,14 +168,22 @@ __device__ __forceinline__ void k_smooth8(float f[8]) {
 // makes the stride (in rows) a multiple of the head count, so the heads of a
 // lane's two rows are the same in every tile it visits: a lane keeps its
 // running maxima (pass 1) and its heads' scales (pass 2) in registers.
-#ifndef MXQ_KV_GRID_BLOCKS
-#define MXQ_KV_GRID_BLOCKS 1024
+// Workgroups of each pass (at most; rounded up as the launcher explains).
+// Pass 1 ends with one atomic per head and workgroup, so it takes fewer.
+#ifndef MXQ_KV_AMAX_GRID_BLOCKS
+#define MXQ_KV_AMAX_GRID_BLOCKS 1024
 #endif
-constexpr int64_t kKvGridBlocks = MXQ_KV_GRID_BLOCKS;
+#ifndef MXQ_KV_QUANT_GRID_BLOCKS
+#define MXQ_KV_QUANT_GRID_BLOCKS 1536
+#endif
+constexpr int64_t kKvAmaxGridBlocks = MXQ_KV_AMAX_GRID_BLOCKS;
+constexpr int64_t kKvQuantGridBlocks = MXQ_KV_QUANT_GRID_BLOCKS;
 #ifndef MXQ_KV_ROW_UNROLL
-#define MXQ_KV_ROW_UNROLL 4
+#define MXQ_KV_ROW_UNROLL 2
 #endif
-constexpr int kKvRowUnroll = MXQ_KV_ROW_UNROLL;        // tiles in flight per wave
+// tiles a wave works on per step; the next step's tiles are loaded before
+// this step's arithmetic, so 2 * kKvRowUnroll tiles are in registers
+constexpr int kKvRowUnroll = MXQ_KV_ROW_UNROLL;
 
 struct KvGeom {
   int64_t nchunks;   // S * H * D / 8
@@ -184,6 +193,9 @@ struct KvGeom {
 
 // Each head's maximum is spread over kKvAmaxSlots words (workgroup b folds
 // into slot b % kKvAmaxSlots), which keeps the atomics on one address few.
+// The scratch is slot-major, word s * H + h, so that the slots of one head
+// lie in different cache lines (atomics on one line serialize); slot 0 of
+// head h, word h, holds the head's maximum after the quantize pass.
 #ifndef MXQ_KV_AMAX_SLOTS
 #define MXQ_KV_AMAX_SLOTS 32
 #endif
@@ -209,13 +221,39 @@ struct KvRows {
 template <int DT>
 struct KvTile { Raw8<DT> c0, c1; };
 
-template <int DT>
+// FULL: every chunk of the tile is in range (no guards, so that the loads and
+// stores of a step are unconditional and the compiler can wait for exactly
+// the loads a step needs while the next step's are in flight).
+template <int DT, bool FULL>
 __device__ __forceinline__ KvTile<DT> kv_tile_load(const void* k, const KvGeom& geo, int64_t tile) {
   const int64_t c = tile * 128 + (threadIdx.x & 63);
   KvTile<DT> t;
-  t.c0 = c < geo.nchunks ? ld8<DT>(k, c) : zero8<DT>();
-  t.c1 = c + 64 < geo.nchunks ? ld8<DT>(k, c + 64) : zero8<DT>();
+  t.c0 = (FULL || c < geo.nchunks) ? ld8<DT>(k, c) : zero8<DT>();
+  t.c1 = (FULL || c + 64 < geo.nchunks) ? ld8<DT>(k, c + 64) : zero8<DT>();
   return t;
+}
+
+// Whether tiles tile, tile + stride, ..., tile + (n - 1) * stride all lie
+// wholly in range (uniform over the wave).
+__device__ __forceinline__ bool kv_tiles_full(const KvGeom& geo, int64_t tile, int64_t stride, int n) {
+  return (tile + (n - 1) * stride) * 128 + 128 <= geo.nchunks;
+}
+
+// Pass 1 on one tile: the running maxima of the lane's two rows.
+template <int DT, bool SMOOTH, int L>
+__device__ __forceinline__ void kv_amax_tile(const KvTile<DT>& t, float& m0, float& m1) {
+  float f0[8], f1[8];
+  unpack8<DT>(t.c0, f0);
+  unpack8<DT>(t.c1, f1);
+  if constexpr (SMOOTH) {
+    k_smooth8<DT, L>(f0);
+    k_smooth8<DT, L>(f1);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    m0 = fmaxf(m0, fabsf(f0[i]));
+    m1 = fmaxf(m1, fabsf(f1[i]));
+  }
 }
 
 template <int DT, bool SMOOTH, int L>
@@ -226,27 +264,32 @@ __global__ __launch_bounds__(256) void k_kv_head_amax(const void* __restrict__ k
   for (int i = threadIdx.x; i < geo.H; i += blockDim.x) s_max[i] = 0u;
   __syncthreads();
   const KvRows<L> rr(geo);
+  const int64_t st = rr.stride;
   float m0 = 0.0f, m1 = 0.0f;           // running maxima of the lane's two rows' heads
   // chunks past the end load as zeros, which leave a maximum unchanged
-  for (int64_t tile = rr.tile; tile < geo.tiles; tile += U * rr.stride) {   // uniform
-    KvTile<DT> t[U];
+  KvTile<DT> t[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT>(k, geo, tile + u * rr.stride);
+  for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT, false>(k, geo, rr.tile + u * st);
+  // the next step's loads go out before this step's arithmetic; steps whose
+  // next tiles are all in range first (one loop without guards), then the rest
+  int64_t tile = rr.tile;
+  for (; tile < geo.tiles && kv_tiles_full(geo, tile + U * st, st, U); tile += U * st) {
+    KvTile<DT> n[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float f0[8], f1[8];
-      unpack8<DT>(t[u].c0, f0);
-      unpack8<DT>(t[u].c1, f1);
-      if constexpr (SMOOTH) {
-        k_smooth8<DT, L>(f0);
-        k_smooth8<DT, L>(f1);
-      }
+    for (int u = 0; u < U; ++u) n[u] = kv_tile_load<DT, true>(k, geo, tile + (U + u) * st);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        m0 = fmaxf(m0, fabsf(f0[i]));
-        m1 = fmaxf(m1, fabsf(f1[i]));
-      }
-    }
+    for (int u = 0; u < U; ++u) kv_amax_tile<DT, SMOOTH, L>(t[u], m0, m1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[u] = n[u];
+  }
+  for (; tile < geo.tiles; tile += U * st) {
+    KvTile<DT> n[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) n[u] = kv_tile_load<DT, false>(k, geo, tile + (U + u) * st);
+#pragma unroll
+    for (int u = 0; u < U; ++u) kv_amax_tile<DT, SMOOTH, L>(t[u], m0, m1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[u] = n[u];
   }
   m0 = group_max<L>(m0);
   m1 = group_max<L>(m1);
@@ -257,7 +300,56 @@ __global__ __launch_bounds__(256) void k_kv_head_amax(const void* __restrict__ k
   __syncthreads();
   const int slot = blockIdx.x % kKvAmaxSlots;
   for (int i = threadIdx.x; i < geo.H; i += blockDim.x)
-    if (s_max[i] != 0u) atomicMax(&head_amax[i * kKvAmaxSlots + slot], s_max[i]);
+    if (s_max[i] != 0u) atomicMax(&head_amax[slot * geo.H + i], s_max[i]);
+}
+
+// Pass 2 on one tile: k_smooth, block maxima (the block is the lane pair),
+// one block scale per lane (the even lane's for chunk 0's block, the odd
+// lane's for chunk 1's), both reciprocals by one pair exchange, codes, and
+// the stores.  Every lane of a row writes its row scale (the same value).
+template <int DT, bool SMOOTH, int L, bool FULL>
+__device__ __forceinline__ void kv_quant_tile(const KvTile<DT>& t, const KvGeom& geo, int64_t tile,
+                                              float g_a, float g_b, float g_m, double rg_m,
+                                              uint32_t* __restrict__ packed,
+                                              uint8_t* __restrict__ scales,
+                                              float* __restrict__ row_scale) {
+  constexpr int R = 128 / L;
+  const int lane = threadIdx.x & 63;
+  const bool odd = lane & 1;
+  const int64_t c = tile * 128 + lane;
+  float f0[8], f1[8];
+  unpack8<DT>(t.c0, f0);
+  unpack8<DT>(t.c1, f1);
+  if constexpr (SMOOTH) {
+    k_smooth8<DT, L>(f0);
+    k_smooth8<DT, L>(f1);
+  }
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a0 = fmaxf(a0, fabsf(f0[i]));
+    a1 = fmaxf(a1, fabsf(f1[i]));
+  }
+  a0 = bitsf(max(fbits(a0), pair_swap(fbits(a0))));
+  a1 = bitsf(max(fbits(a1), pair_swap(fbits(a1))));
+  uint32_t sb;
+  const double mine = nv_block_recip(odd ? a1 : a0, g_m, rg_m, sb);
+  const double other = pair_swap(mine);
+  const double r0 = odd ? other : mine, r1 = odd ? mine : other;
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f0[i] * r0));
+  const uint32_t w0 = e2m1_pack8_rne(q, 1.0f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f1[i] * r1));
+  const uint32_t w1 = e2m1_pack8_rne(q, 1.0f);
+  const int64_t cm = odd ? c + 64 : c;                // chunk of this lane's block
+  const int64_t row = tile * R + lane / L;
+  if (FULL || c < geo.nchunks) stream_st(w0, packed + c);
+  if (FULL || c + 64 < geo.nchunks) stream_st(w1, packed + c + 64);
+  if (FULL || cm < geo.nchunks) scales[cm >> 1] = (uint8_t)sb;
+  if (FULL || c < geo.nchunks) row_scale[row] = g_a;
+  if (FULL || c + 64 < geo.nchunks) row_scale[row + R / 2] = g_b;
 }
 
 template <int DT, bool SMOOTH, int L>
@@ -273,67 +365,47 @@ __global__ __launch_bounds__(256) void k_kv_quant(const void* __restrict__ k, Kv
   float* s_g = reinterpret_cast<float*>(s_rg + geo.H);
   for (int i = threadIdx.x; i < geo.H; i += blockDim.x) {
     uint32_t m = 0u;
-    for (int j = 0; j < kKvAmaxSlots; ++j) m = max(m, head_amax[i * kKvAmaxSlots + j]);
-    if (blockIdx.x == 0) head_amax[i * kKvAmaxSlots] = m;
+    for (int j = 0; j < kKvAmaxSlots; ++j) m = max(m, head_amax[j * geo.H + i]);
+    if (blockIdx.x == 0) head_amax[i] = m;
     const float g = bitsf(m) / kGlobalDiv;
     s_g[i] = g;
     s_rg[i] = 1.0 / (double)g;
   }
   __syncthreads();
   constexpr int U = kKvRowUnroll;
-  constexpr int R = 128 / L;
-  const int lane = threadIdx.x & 63;
-  const bool odd = lane & 1;
-  const bool first = (lane & (L - 1)) == 0;
+  const bool odd = threadIdx.x & 1;
   const KvRows<L> rr(geo);
-  // the even lane of a pair scales chunk 0's block (row a), the odd lane
-  // chunk 1's block (row b)
+  const int64_t st = rr.stride;
   const float g_a = s_g[rr.h_a], g_b = s_g[rr.h_b];
   const float g_m = odd ? g_b : g_a;
   const double rg_m = s_rg[odd ? rr.h_b : rr.h_a];
-  for (int64_t tile = rr.tile; tile < geo.tiles; tile += U * rr.stride) {   // uniform
-    KvTile<DT> t[U];
+  KvTile<DT> t[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT>(k, geo, tile + u * rr.stride);
+  for (int u = 0; u < U; ++u) t[u] = kv_tile_load<DT, false>(k, geo, rr.tile + u * st);
+  // as in pass 1: steps whose tiles and next tiles are all in range run
+  // without guards, then the rest
+  int64_t tile = rr.tile;
+  for (; tile < geo.tiles && kv_tiles_full(geo, tile, st, 2 * U); tile += U * st) {
+    KvTile<DT> n[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t tu = tile + u * rr.stride;
-      const int64_t c = tu * 128 + lane;
-      float f0[8], f1[8];
-      unpack8<DT>(t[u].c0, f0);
-      unpack8<DT>(t[u].c1, f1);
-      if constexpr (SMOOTH) {
-        k_smooth8<DT, L>(f0);
-        k_smooth8<DT, L>(f1);
-      }
-      // block maxima of both chunks (the block is this lane pair)
-      float a0 = 0.0f, a1 = 0.0f;
+    for (int u = 0; u < U; ++u) n[u] = kv_tile_load<DT, true>(k, geo, tile + (U + u) * st);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        a0 = fmaxf(a0, fabsf(f0[i]));
-        a1 = fmaxf(a1, fabsf(f1[i]));
-      }
-      a0 = bitsf(max(fbits(a0), pair_swap(fbits(a0))));
-      a1 = bitsf(max(fbits(a1), pair_swap(fbits(a1))));
-      uint32_t sb;
-      const double mine = nv_block_recip(odd ? a1 : a0, g_m, rg_m, sb);
-      const double other = pair_swap(mine);
-      const double r0 = odd ? other : mine, r1 = odd ? mine : other;
-      float q[8];
+    for (int u = 0; u < U; ++u)
+      kv_quant_tile<DT, SMOOTH, L, true>(t[u], geo, tile + u * st, g_a, g_b, g_m, rg_m,
+                                         packed, scales, row_scale);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f0[i] * r0));
-      const uint32_t w0 = e2m1_pack8_rne(q, 1.0f);
+    for (int u = 0; u < U; ++u) t[u] = n[u];
+  }
+  for (; tile < geo.tiles; tile += U * st) {
+    KvTile<DT> n[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f1[i] * r1));
-      const uint32_t w1 = e2m1_pack8_rne(q, 1.0f);
-      const int64_t cm = odd ? c + 64 : c;                // chunk of this lane's block
-      if (c < geo.nchunks) stream_st(w0, packed + c);
-      if (c + 64 < geo.nchunks) stream_st(w1, packed + c + 64);
-      if (cm < geo.nchunks) scales[cm >> 1] = (uint8_t)sb;
-      const int64_t row = tu * R + lane / L;
-      if (first && c < geo.nchunks) row_scale[row] = g_a;
-      if (first && c + 64 < geo.nchunks) row_scale[row + R / 2] = g_b;
-    }
+    for (int u = 0; u < U; ++u) n[u] = kv_tile_load<DT, false>(k, geo, tile + (U + u) * st);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      kv_quant_tile<DT, SMOOTH, L, false>(t[u], geo, tile + u * st, g_a, g_b, g_m, rg_m,
+                                          packed, scales, row_scale);
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[u] = n[u];
   }
 }
 
@@ -343,19 +415,19 @@ __global__ void k_fill_head_amax(uint32_t* p, int n) {
 }
 
 template <int DT, bool SMOOTH, int L>
-static void launch_kv_quant_l(const void* k, const KvGeom& geo, int64_t nblk,
+static void launch_kv_quant_l(const void* k, const KvGeom& geo, const int64_t nblk[2],
                               uint32_t* head_amax, uint32_t* packed, uint8_t* scales,
                               float* row_scale, hipStream_t s) {
   const size_t lds_max = sizeof(uint32_t) * (size_t)geo.H;
   const size_t lds_g = (sizeof(double) + sizeof(float)) * (size_t)geo.H;
-  hipLaunchKernelGGL((k_kv_head_amax<DT, SMOOTH, L>), dim3((unsigned)nblk), dim3(256), lds_max, s,
+  hipLaunchKernelGGL((k_kv_head_amax<DT, SMOOTH, L>), dim3((unsigned)nblk[0]), dim3(256), lds_max, s,
                      k, geo, head_amax);
-  hipLaunchKernelGGL((k_kv_quant<DT, SMOOTH, L>), dim3((unsigned)nblk), dim3(256), lds_g, s, k,
+  hipLaunchKernelGGL((k_kv_quant<DT, SMOOTH, L>), dim3((unsigned)nblk[1]), dim3(256), lds_g, s, k,
                      geo, head_amax, packed, scales, row_scale);
 }
 
 template <int DT, bool SMOOTH>
-static void launch_kv_quant_d(const void* k, const KvGeom& geo, int64_t nblk, int64_t D,
+static void launch_kv_quant_d(const void* k, const KvGeom& geo, const int64_t nblk[2], int64_t D,
                               uint32_t* ha, uint32_t* p, uint8_t* sc, float* rs, hipStream_t s) {
   switch (D) {     // chunks (lanes) per row
     case 16: launch_kv_quant_l<DT, SMOOTH, 2>(k, geo, nblk, ha, p, sc, rs, s); break;
@@ -368,7 +440,7 @@ static void launch_kv_quant_d(const void* k, const KvGeom& geo, int64_t nblk, in
 }
 
 template <int DT>
-static void launch_kv_quant_dt(const void* k, const KvGeom& geo, int64_t nblk, int64_t D,
+static void launch_kv_quant_dt(const void* k, const KvGeom& geo, const int64_t nblk[2], int64_t D,
                                bool smooth, uint32_t* ha, uint32_t* p, uint8_t* sc, float* rs,
                                hipStream_t s) {
   if (smooth) launch_kv_quant_d<DT, true>(k, geo, nblk, D, ha, p, sc, rs, s);
@@ -382,16 +454,21 @@ hipError_t launch_kv_quant(const void* k, int dt, int64_t S, int64_t H, int64_t 
   geo.nchunks = S * H * (D / 8);
   geo.tiles = (geo.nchunks + 127) / 128;
   geo.H = (int)H;
-  // workgroups: about kKvGridBlocks (fewer for small tensors), a multiple of
-  // q = H / gcd(4 * rows per tile, H), so that the stride of the grid's
-  // 4 * nblk waves, 4 * nblk * rows per tile rows, is a multiple of H
+  // workgroups of each pass: up to its cap (fewer for small tensors), then
+  // rounded up to a multiple of q = H / gcd(4 * rows per tile, H), so that
+  // the stride of the grid's 4 * nblk waves, 4 * nblk * rows per tile rows,
+  // is a multiple of H
   const int64_t rows_per_tile = 1024 / D;
   int64_t a = 4 * rows_per_tile, b = H;
   while (b != 0) { const int64_t r = a % b; a = b; b = r; }
   const int64_t q = H / a;
-  int64_t nblk = (geo.tiles + 3) / 4;
-  nblk = nblk < kKvGridBlocks ? nblk : kKvGridBlocks;
-  nblk = (nblk + q - 1) / q * q;
+  const int64_t want = (geo.tiles + 3) / 4;
+  const int64_t caps[2] = {kKvAmaxGridBlocks, kKvQuantGridBlocks};
+  int64_t nblk[2];
+  for (int i = 0; i < 2; ++i) {
+    const int64_t n = want < caps[i] ? want : caps[i];
+    nblk[i] = (n + q - 1) / q * q;
+  }
   uint32_t* ha = reinterpret_cast<uint32_t*>(head_amax);
   const int nslots = (int)H * kKvAmaxSlots;
   hipLaunchKernelGGL(k_fill_head_amax, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, ha, nslots);

@@ -275,8 +275,8 @@ mxq_status mxq_dequantize_kv_pages_nvfp4(const uint8_t* const* values,
  *              1 / head_dim, rounded to dt; value - mean evaluated in binary32
  *              and rounded to dt.  0: no smoothing (values).  Else MXQ_E_MODE.
  *   head_amax  [heads * 32] float32 device scratch (each head's maximum is
- *              gathered in 32 slots); after the call head_amax[h * 32] holds
- *              head h's amax (of the smoothed values).
+ *              gathered in 32 slots, slot-major); after the call head_amax[h]
+ *              holds head h's amax (of the smoothed values).
  *   packed     uint8 [tokens, heads, head_dim / 2] (16-byte aligned),
  *   scales     e4m3 bytes [tokens, heads, head_dim / 16],
  *   row_scale  float32 [tokens, heads]: the head's g = amax / (6 * 448) on each

@@ -124,7 +124,7 @@ def gpu_quantize_kv(k, smooth):
     ha = torch.full((H * 32,), 123.0, dtype=torch.float32, device=DEV)   # stale scratch
     mxq().mxq_quantize_kv_nvfp4(k, ha, p, s, g, smooth)
     check_guard(rp); check_guard(rs); check_guard(rg)
-    return p, s, g, ha[::32]
+    return p, s, g, ha[:H]
 
 
 KV_SHAPES = [(40, 3, 128), (1000, 12, 128), (7, 5, 16), (33, 2, 512), (64, 4, 64), (17, 1, 32),
