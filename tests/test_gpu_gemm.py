@@ -178,15 +178,18 @@ def _byte_weights(fmt, E, N, K, seed):
     return (p, s, g), oracle.dequantize_nvfp4(p, s, g, torch.bfloat16)
 
 
+@pytest.mark.parametrize("shape", [(2, 128, 256), (2, 256, 512)])
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("transpose", [False, True])
-def test_grouped_mm_one_hot_reproduces_dequantized_weights(fmt, transpose):
+def test_grouped_mm_one_hot_reproduces_dequantized_weights(fmt, transpose, shape):
     """With one-hot activation rows every output is one weight times 1.0 plus
     zeros, so the GEMM must return the dequantized weights exactly: W_e^T in
     the forward (rows over k), W_e in the backward (rows over n).  This pins
     the in-register dequantization to the dequantize definition bit for bit
-    (zeros compared as values: their sign follows the accumulation)."""
-    E, N, K = 2, 128, 256
+    (zeros compared as values: their sign follows the accumulation).  The
+    second shape spans two output tiles and several reduction steps in both
+    directions."""
+    E, N, K = shape
     q, wd = _byte_weights(fmt, E, N, K, seed=38)
     R = N if transpose else K
     x = torch.eye(R, dtype=torch.bfloat16).repeat(E, 1)
