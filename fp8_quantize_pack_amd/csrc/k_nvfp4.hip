@@ -371,10 +371,12 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant_seg(
   }
 }
 
-// Segments a wave may hold in registers (1, 2, 4, or 8 when built so); rows
-// needing more than 4 waves x this many segments take the two-pass fallback.
+// Segments a wave may hold in registers (1, 2, 4 or 8; 8 by default, so that
+// one wave owns a whole row of up to 8192 columns: no LDS exchange, no
+// barrier, no wave idling on a shorter share of the row); rows needing more
+// than 4 waves x this many segments take the two-pass fallback.
 #ifndef MXQ_NV_MAX_NIT
-#define MXQ_NV_MAX_NIT 4
+#define MXQ_NV_MAX_NIT 8
 #endif
 
 template <int DT, int WPR, bool FULL>
