@@ -10,12 +10,15 @@ One step = one pass of the whole path over resident synthetic inputs:
     fp8 block 32 [16, 8192, 512], mxfp4 block 32 [16, 8192, 128], nvfp4 block
     16 [16, 2048, 512].
 `value` is effective GB/s: algorithmic bytes (every input read once plus every
-output written once) of the whole step divided by the step's wall time.
+output written once) of the whole step divided by the step's wall time.  The
+timed steps replay the step's launches captured once as a HIP graph (the same
+kernels with the same arguments, without host launch gaps between them);
+`--eager` times eager launches instead, and `eager_GBps` always reports them.
 
 Prints one JSON line.  Also reports, per kernel, its average launch duration
-from HIP events recorded on the launch stream, the roofline of the dominant
-kernel against MI355X's 8 TB/s HBM peak, and the CPU oracle timed on a bounded
-sample of the same workload.
+from HIP events recorded on the launch stream (eager launches), the roofline of
+the dominant kernel against MI355X's 8 TB/s HBM peak, and the CPU oracle timed
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -48,6 +51,8 @@ def parse():
                     help="skip the grouped-GEMM measurement (not part of `value`)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the MXFP8 / static FP4 / KV-cache measurements (not part of `value`)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as eager launches instead of HIP graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a torch negation over one 36-expert chunk "
                          "(reads and writes CALIBRATION_BYTES) for HBM counter calibration")
@@ -148,7 +153,8 @@ def main():
         run_step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronized on both sides
+    # per-launch durations: K eager steps with HIP events around every launch
+    # (on the stream the kernels run on)
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
            for _ in plan] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -156,8 +162,30 @@ def main():
     for s in range(args.steps):
         run_step(ev[s])
     torch.cuda.synchronize()
+    eager_wall = time.perf_counter() - t0
+    progress(f"{args.steps} eager steps with per-launch events: {eager_wall:.3f} s")
+
+    # the step as one HIP graph: the same launches with the same arguments,
+    # replayed without host launch gaps between them
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_step()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronized on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    progress(f"{args.steps} timed steps: {wall:.3f} s")
+    progress(f"{args.steps} timed steps ({'graph replays' if graph is not None else 'eager'}): {wall:.3f} s")
 
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
@@ -216,7 +244,9 @@ def main():
         "config": {"workload": "MoE expert sweep bf16 [%d,2048,7168] in 36-expert chunks: MXFP4 + NVFP4 "
                                "quantize-pack and dequantize to bf16; plus cache QDQ fp8/b32 [16,8192,512], "
                                "mxfp4/b32 [16,8192,128], nvfp4/b16 [16,2048,512]" % E,
-                   "parallelism": "single GPU", "chunks": len(chunks), "step_bytes": step_bytes},
+                   "parallelism": "single GPU", "chunks": len(chunks), "step_bytes": step_bytes,
+                   "launch": "eager" if graph is None else "hip_graph (one step captured, replayed K times)"},
+        "eager_GBps": round(step_bytes * args.steps / eager_wall / 1e9, 1),
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "fp4_sweep_GBps": round(fp4_bytes / (fp4_ms * 1e-3) / 1e9, 1),
         "roofline": roofline,
