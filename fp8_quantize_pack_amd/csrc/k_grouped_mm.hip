@@ -266,6 +266,9 @@ __global__ __launch_bounds__(THREADS) MXQ_GMM_OCCUPANCY void k_grouped_mm(Args a
     store_stage<FMT, TRANS, BM>(st, As, Bs, tid);
     __syncthreads();
     if (r0 + BK < R) load_stage<FMT, TRANS, BM>(a, st, tid, e, m0, m1, c0, r0 + BK, R);
+    // backward: LLVM's MFMA-interleaving schedule (iglp strategy 1) measured
+    // 2-4% faster for MXFP4; for the forward product it is 27% slower
+    if constexpr (TRANS == 1) __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       bf16x8 af[MT], bfr[2];
