@@ -508,6 +508,26 @@ def test_full_c3_nvfp4_gate_up(given_half):
     assert_same(y.reshape(-1, K)[idx], oracle.dequantize_nvfp4(po, so, go, torch.bfloat16), "dequant")
 
 
+def test_full_nvfp4_tensor_mode_sweep_chunk():
+    """Per-tensor NVFP4 on the workload the bench times for it: one 36-expert
+    chunk of the MoE sweep as rows of 4096 (1 GB, the whole-tensor amax pass
+    on one workgroup per CU).  The tensor amax is compared whole (against
+    torch's exact maximum), every row scale must be amax / 2688 rounded once,
+    and sampled rows against the oracle with that given scale (the oracle's
+    tensor mode is its given mode with g = amax / 2688, a pinned identity)."""
+    say("full nvfp4 tensor mode [129024, 4096]")
+    x = synth.c5_chunk(0, synth.C5_CHUNK_EXPERTS, device=DEV).reshape(-1, 4096)
+    p, s, g = gpu_quantize_nvfp4(x, mode="tensor")
+    amax = x.abs().max().float().cpu().numpy()
+    g0 = np.float32(amax) / np.float32(2688.0)
+    assert torch.equal(g.cpu(), torch.full_like(g.cpu(), float(g0))), "row scales"
+    idx = _sample_rows(x.shape[0], 1500, 6).to(DEV)
+    po, so, go = oracle.quantize_nvfp4(x[idx].cpu(), mode="given",
+                                       given=torch.full((idx.numel(),), float(g0)))
+    assert_same(s[idx], so, "scales")
+    assert_same(p[idx], po, "packed")
+
+
 @pytest.mark.parametrize("case,fmt,B", [("c4a", "fp8", 32), ("c4b", "mxfp4", 32), ("c4c", "nvfp4", 16)])
 def test_full_c4_cache(case, fmt, B):
     say("full", case, fmt)
