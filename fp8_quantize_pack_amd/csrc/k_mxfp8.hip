@@ -101,12 +101,6 @@ __global__ __launch_bounds__(64 * kMx8Waves) void k_mxfp8_quant(
   }
 }
 
-// float32 value of an e8m0 byte: 2^(b - 127); byte 0 is the subnormal
-// 2^-127, byte 255 is NaN.
-__device__ __forceinline__ float e8m0_value(uint32_t b) {
-  const float v = (b == 0u) ? bitsf(0x00400000u) : bitsf(b << 23);
-  return (b == 255u) ? bitsf(0x7FC00000u) : v;
-}
 
 template <int DT>
 __global__ __launch_bounds__(64 * kMx8Waves) void k_mxfp8_dequant(
@@ -129,12 +123,20 @@ __global__ __launch_bounds__(64 * kMx8Waves) void k_mxfp8_dequant(
 #pragma unroll
     for (int u = 0; u < kMx8Unroll; ++u) {
       const int64_t c = c0 + u * kWave;
-      const float s = e8m0_value(sb[u]);
+      // e4m3 * 2^(b - 127) through the scaled fp8 converter, two codes per
+      // instruction: the product of a 4-bit significand at or above 2^-9 and a
+      // power of two at or above 2^-127 is an exact float32 (lowest bit >=
+      // 2^-136), so the converter's result is exact; byte 255 is NaN.
+      const float sc = e8m0_as_scale(sb[u]);
       float f[8];
+      f32x2 v;
+      v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[u].x, sc, false); f[0] = v.x; f[1] = v.y;
+      v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[u].x, sc, true);  f[2] = v.x; f[3] = v.y;
+      v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[u].y, sc, false); f[4] = v.x; f[5] = v.y;
+      v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[u].y, sc, true);  f[6] = v.x; f[7] = v.y;
+      if (sb[u] == 255u) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t byte = ((i < 4 ? w[u].x : w[u].y) >> (8 * (i & 3))) & 0xFFu;
-        f[i] = e4m3_decode_any(byte) * s;        // exact unless it overflows
+        for (int i = 0; i < 8; ++i) f[i] = bitsf(0x7FC00000u);
       }
       if (c < nchunks) st8<DT>(y, c, f);
     }
