@@ -95,6 +95,7 @@ __device__ __forceinline__ void cache_chunk(const Raw8<DT>& raw, bool ok, void* 
 #define MXQ_CACHE_UNROLL 2
 #endif
 constexpr int kCacheUnroll = MXQ_CACHE_UNROLL;
+constexpr int64_t kCacheGroupsPerWave = 2 * kCacheUnroll;
 
 template <int DT, int FMT, int B>
 __global__ __launch_bounds__(256) void k_cache_qdq(const void* __restrict__ x,
@@ -169,9 +170,14 @@ static hipError_t launch_fast(const void* x, void* y, const CacheGeom& geo,
                               int B, hipStream_t s) {
   const int64_t rows_per_wave = kWave / geo.lpr;
   const int64_t waves = (geo.rows + rows_per_wave - 1) / rows_per_wave;
-  const int64_t max_blocks = kCacheGridBlocks;
-  int64_t b = (waves + 3) / 4;
-  const dim3 grid((unsigned)(b < max_blocks ? (b > 0 ? b : 1) : max_blocks)), block(256);
+  // about kCacheGroupsPerWave row groups per wave (two steps of kCacheUnroll):
+  // measured best on 32 MiB to 128 MiB tensors over fixed grid caps, which
+  // favoured small tensors or large ones but not both
+  int64_t b = (waves + 4 * kCacheGroupsPerWave - 1) / (4 * kCacheGroupsPerWave);
+  b = b < kCacheGridBlocks ? kCacheGridBlocks : b;
+  b = b < (waves + 3) / 4 ? b : (waves + 3) / 4;
+  b = b < kMaxGridBlocks ? (b > 0 ? b : 1) : kMaxGridBlocks;
+  const dim3 grid((unsigned)b), block(256);
   switch (B) {
     case 8: hipLaunchKernelGGL((k_cache_qdq<DT, FMT, 8>), grid, block, 0, s, x, y, geo); break;
     case 16: hipLaunchKernelGGL((k_cache_qdq<DT, FMT, 16>), grid, block, 0, s, x, y, geo); break;

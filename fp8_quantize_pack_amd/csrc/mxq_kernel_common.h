@@ -18,8 +18,9 @@ constexpr int kWave = 64;
 // the chip at once the dispatcher hands out work as CUs free up, which
 // balances the XCDs and leaves no tail of workgroups that did not fit in the
 // first round (a grid of exactly the resident count is right only while the
-// register budget allows that many).  The cache kernels, with much smaller
-// tensors, use at most kCacheGridBlocks.
+// register budget allows that many).  The cache kernels give each wave a few
+// row groups, with at least kCacheGridBlocks workgroups when there is work
+// for that many.
 #ifndef MXQ_BLOCKS_PER_CU
 #define MXQ_BLOCKS_PER_CU 1024
 #endif
