@@ -99,7 +99,10 @@ hipError_t launch_kv_pages_dequant(const uint8_t* const* values, const uint8_t* 
   const int64_t cpb = block_tokens * H * (D / 8);
   const int64_t tpb = (cpb + kKvTileChunks - 1) / kKvTileChunks;
   const int64_t ntiles = tpb * nblocks;
-  int64_t g = (ntiles + 3) / 4;
+#ifndef MXQ_KVP_UPW
+#define MXQ_KVP_UPW MXQ_UNITS_PER_WAVE
+#endif
+  int64_t g = (ntiles + 4 * MXQ_KVP_UPW - 1) / (4 * MXQ_KVP_UPW);
   g = g < kMaxGridBlocks ? (g > 0 ? g : 1) : kMaxGridBlocks;
   const dim3 grid((unsigned)g), block(256);
   switch (dt) {

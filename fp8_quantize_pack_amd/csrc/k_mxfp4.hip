@@ -128,7 +128,10 @@ __global__ __launch_bounds__(64 * kMxWaves) void k_mxfp4_dequant(
 static int grid_for(int64_t ntiles) {
   // One tile per wave, kMxWaves waves per workgroup, up to the grid cap.
   const int64_t max_blocks = kMaxGridBlocks;
-  int64_t b = (ntiles + kMxWaves - 1) / kMxWaves;
+#ifndef MXQ_MX_UPW
+#define MXQ_MX_UPW MXQ_UNITS_PER_WAVE
+#endif
+  int64_t b = (ntiles + kMxWaves * MXQ_MX_UPW - 1) / (kMxWaves * MXQ_MX_UPW);
   return (int)(b < max_blocks ? (b > 0 ? b : 1) : max_blocks);
 }
 

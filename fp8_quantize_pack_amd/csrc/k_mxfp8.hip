@@ -144,7 +144,10 @@ __global__ __launch_bounds__(64 * kMx8Waves) void k_mxfp8_dequant(
 }
 
 static int mx8_grid(int64_t ntiles) {
-  int64_t b = (ntiles + kMx8Waves - 1) / kMx8Waves;
+#ifndef MXQ_MX8_UPW
+#define MXQ_MX8_UPW MXQ_UNITS_PER_WAVE
+#endif
+  int64_t b = (ntiles + kMx8Waves * MXQ_MX8_UPW - 1) / (kMx8Waves * MXQ_MX8_UPW);
   return (int)(b < kMaxGridBlocks ? (b > 0 ? b : 1) : kMaxGridBlocks);
 }
 

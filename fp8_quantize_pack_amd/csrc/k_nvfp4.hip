@@ -417,6 +417,12 @@ static void launch_seg(int nit, int wpr, dim3 grid, hipStream_t s, const void* x
   }
 }
 
+#ifndef MXQ_NVQ_UPW
+#define MXQ_NVQ_UPW MXQ_UNITS_PER_WAVE
+#endif
+#ifndef MXQ_NVD_UPW
+#define MXQ_NVD_UPW MXQ_UNITS_PER_WAVE
+#endif
 static dim3 grid_of(int64_t units) {
   return dim3((unsigned)(units < kMaxGridBlocks ? (units > 0 ? units : 1) : kMaxGridBlocks));
 }
@@ -443,7 +449,7 @@ hipError_t launch_nvfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
     int lpr = 1;
     while (lpr < bpr) lpr <<= 1;
     const int64_t rows_per_block = 4 * (kWave / lpr);
-    const dim3 grid = grid_of((rows + rows_per_block - 1) / rows_per_block);
+    const dim3 grid = grid_of(((rows + rows_per_block - 1) / rows_per_block + MXQ_NVQ_UPW - 1) / MXQ_NVQ_UPW);
     u32x2* p = reinterpret_cast<u32x2*>(packed);
     switch (dt) {
       case DT_F32: hipLaunchKernelGGL(k_nvfp4_quant_short<DT_F32>, grid, dim3(256), 0, s, x, rows, bpr, lpr, mode, given, given_stride, ta, p, scales, row_scale); break;
@@ -466,7 +472,7 @@ hipError_t launch_nvfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
   while (nit < per_wave) nit <<= 1;
   if (nit > MXQ_NV_MAX_NIT) { nit = 0; wpr = 4; }         // two passes over the row
   const int64_t rows_per_block = 4 / wpr;
-  const dim3 grid = grid_of((rows + rows_per_block - 1) / rows_per_block);
+  const dim3 grid = grid_of(((rows + rows_per_block - 1) / rows_per_block + MXQ_NVQ_UPW - 1) / MXQ_NVQ_UPW);
   uint32_t* p = reinterpret_cast<uint32_t*>(packed);
   switch (dt) {
     case DT_F32: launch_seg<DT_F32>(nit, wpr, grid, s, x, geo, mode, given, given_stride, ta, p, scales, row_scale); break;
@@ -482,7 +488,7 @@ hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales,
   const int64_t cpr = K / 8;
   if (cpr >= kDqSegChunks) {
     const int64_t nseg = (cpr + kDqSegChunks - 1) / kDqSegChunks;
-    const dim3 grid = grid_of((rows * nseg + 3) / 4), block(256);
+    const dim3 grid = grid_of((rows * nseg + 4 * MXQ_NVD_UPW - 1) / (4 * MXQ_NVD_UPW)), block(256);
     const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
     switch (dt) {
       case DT_F32: hipLaunchKernelGGL(k_nvfp4_dequant_seg<DT_F32>, grid, block, 0, s, p, scales, row_scale, rows, cpr, nseg, y); break;
@@ -497,7 +503,7 @@ hipError_t launch_nvfp4_dequant(const uint8_t* packed, const uint8_t* scales,
   geo.ntiles = (geo.nchunks + kDqFlatTile - 1) / kDqFlatTile;
   geo.drow = (int32_t)(kWave / cpr);
   geo.drem = (int32_t)(kWave % cpr);
-  const dim3 grid = grid_of((geo.ntiles + 3) / 4), block(256);
+  const dim3 grid = grid_of((geo.ntiles + 4 * MXQ_NVD_UPW - 1) / (4 * MXQ_NVD_UPW)), block(256);
   const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
   switch (dt) {
     case DT_F32: hipLaunchKernelGGL(k_nvfp4_dequant_flat<DT_F32>, grid, block, 0, s, p, scales, row_scale, geo, y); break;

@@ -29,6 +29,13 @@ constexpr int64_t kMaxGridBlocks = 256 * MXQ_BLOCKS_PER_CU;
 #define MXQ_CACHE_BLOCKS_PER_CU 8
 #endif
 constexpr int64_t kCacheGridBlocks = 256 * MXQ_CACHE_BLOCKS_PER_CU;
+// Work units (wave tiles or row groups) each wave of a streaming kernel takes
+// in turn; the grid has units / (units per wave) waves.  One unit per wave
+// measured fastest for every kernel but the static FP4 round trip (which
+// sets its own).
+#ifndef MXQ_UNITS_PER_WAVE
+#define MXQ_UNITS_PER_WAVE 1
+#endif
 
 // Streaming inputs and outputs are touched once: their global accesses carry
 // the non-temporal hint unless MXQ_TEMPORAL is defined.
