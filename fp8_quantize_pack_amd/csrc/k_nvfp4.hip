@@ -379,21 +379,50 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant_seg(
 #define MXQ_NV_MAX_NIT 8
 #endif
 
+// A row kernel holding 5 to 8 segments per wave runs four of its workgroups
+// per CU, one wave per SIMD each (see occupancy_lds): on the MoE sweep (rows
+// of 7168 columns, 7 segments) it ran at 199 us per 36-expert chunk with four
+// waves per SIMD, 209 with five (what its registers allow) and 216 with
+// three.  With 4 segments (rows of 4096) it ran 2% faster uncapped.
+#ifndef MXQ_NV_SEG_WG_PER_CU
+#define MXQ_NV_SEG_WG_PER_CU 4
+#endif
+constexpr unsigned kNvSegOccupancyLds = occupancy_lds(MXQ_NV_SEG_WG_PER_CU);
+
+template <int DT, int NIT, int WPR, bool FULL>
+static void launch_seg_k(dim3 grid, hipStream_t s, const void* x, const NvSegGeom& geo,
+                         int mode, const float* given, int64_t gs, const uint32_t* ta,
+                         uint32_t* p, uint8_t* sc, float* rs) {
+  const unsigned lds = NIT >= 5 ? kNvSegOccupancyLds : 0u;
+  hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, NIT, WPR, FULL>), grid, dim3(256), lds, s, x,
+                     geo, mode, given, gs, ta, p, sc, rs);
+}
+
+// Every segment count a wave can hold has its own instantiation, so no wave
+// keeps registers for, or computes, a segment past the end of its row (at
+// K = 7168, 7 segments in 8 slots took 2% longer).  Waves that share a row
+// hold more than MXQ_NV_MAX_NIT / 2 segments, since shorter rows take fewer
+// waves; any count without a kernel here goes to NIT = 0, which serves every
+// row length.
 template <int DT, int WPR, bool FULL>
 static void launch_seg_f(int nit, dim3 grid, hipStream_t s, const void* x,
                          const NvSegGeom& geo, int mode, const float* given,
                          int64_t gs, const uint32_t* ta, uint32_t* p,
                          uint8_t* sc, float* rs) {
-  const dim3 block(256);
+#define MXQ_SEG_CASE(n)                                                              \
+  case n:                                                                            \
+    if constexpr (n <= MXQ_NV_MAX_NIT && (WPR == 1 || 2 * n > MXQ_NV_MAX_NIT)) {      \
+      launch_seg_k<DT, n, WPR, FULL>(grid, s, x, geo, mode, given, gs, ta, p, sc, rs); \
+      return;                                                                        \
+    }                                                                                \
+    break;
   switch (nit) {
-    case 1: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 1, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
-    case 2: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 2, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
-    case 4: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 4, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
-#if MXQ_NV_MAX_NIT >= 8
-    case 8: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 8, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
-#endif
-    default: hipLaunchKernelGGL((k_nvfp4_quant_seg<DT, 0, WPR, FULL>), grid, block, 0, s, x, geo, mode, given, gs, ta, p, sc, rs); break;
+    MXQ_SEG_CASE(1) MXQ_SEG_CASE(2) MXQ_SEG_CASE(3) MXQ_SEG_CASE(4)
+    MXQ_SEG_CASE(5) MXQ_SEG_CASE(6) MXQ_SEG_CASE(7) MXQ_SEG_CASE(8)
+    default: break;
   }
+#undef MXQ_SEG_CASE
+  launch_seg_k<DT, 0, WPR, FULL>(grid, s, x, geo, mode, given, gs, ta, p, sc, rs);
 }
 
 template <int DT, int WPR>
@@ -464,12 +493,10 @@ hipError_t launch_nvfp4_quant(const void* x, int dt, int64_t rows, int64_t K,
   geo.cpr = 2 * bpr;
   geo.nseg = (int)((bpr + 63) / 64);
   // waves per row: the fewest (1, 2, 4) that leave each wave at most
-  // MXQ_NV_MAX_NIT segments; NIT = that count rounded up to a power of two.
+  // MXQ_NV_MAX_NIT segments; NIT = that many segments per wave.
   int wpr = 1;
   while (wpr < 4 && geo.nseg > MXQ_NV_MAX_NIT * wpr) wpr <<= 1;
-  const int per_wave = (geo.nseg + wpr - 1) / wpr;
-  int nit = 1;
-  while (nit < per_wave) nit <<= 1;
+  int nit = (geo.nseg + wpr - 1) / wpr;
   if (nit > MXQ_NV_MAX_NIT) { nit = 0; wpr = 4; }         // two passes over the row
   const int64_t rows_per_block = 4 / wpr;
   const dim3 grid = grid_of(((rows + rows_per_block - 1) / rows_per_block + MXQ_NVQ_UPW - 1) / MXQ_NVQ_UPW);

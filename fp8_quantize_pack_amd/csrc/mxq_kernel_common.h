@@ -37,6 +37,12 @@ constexpr int64_t kCacheGridBlocks = 256 * MXQ_CACHE_BLOCKS_PER_CU;
 #define MXQ_UNITS_PER_WAVE 1
 #endif
 
+// Dynamic LDS to ask for at launch, never touched by the kernel, so that at
+// most `wg` workgroups share a CU's 160 KB (a multiple of the 512-byte LDS
+// allocation granule).  Registers alone let most streaming kernels run eight
+// waves per SIMD; the two quantizers that measured faster with fewer take this.
+constexpr unsigned occupancy_lds(unsigned wg) { return (160u * 1024u / wg) & ~511u; }
+
 // Streaming inputs and outputs are touched once: their global accesses carry
 // the non-temporal hint unless MXQ_TEMPORAL is defined.
 template <typename T>

@@ -36,7 +36,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 BENCH_KERNELS = {
     "mxfp4_quant": "mxq::k_mxfp4_quant<1>",
     "mxfp4_dequant": "mxq::k_mxfp4_dequant<1>",
-    "nvfp4_quant": "mxq::k_nvfp4_quant_seg<1, 8, 1, true>",
+    "nvfp4_quant": "mxq::k_nvfp4_quant_seg<1, 7, 1, true>",
     "nvfp4_dequant": "mxq::k_nvfp4_dequant_seg<1>",
     "cache_fp8": "mxq::k_cache_qdq<1, 0, 32>",
     "cache_mxfp4": "mxq::k_cache_qdq<1, 1, 32>",

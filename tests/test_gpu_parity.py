@@ -269,8 +269,12 @@ def test_mxfp4_empty_inputs_launch_nothing():
 
 # ------------------------------------------------------------------ NVFP4
 
-NV_SHAPES = [(5, 16), (7, 48), (33, 512), (4, 1008), (3, 1040), (9, 2064), (6, 4096), (5, 7168),
-             (3, 8208), (2, 16400), (2, 3, 256)]
+# Row lengths cover every segment count a wave holds (1 to 8 with one wave
+# per row; 5 to 8 with two and four), full and ragged last segments, and the
+# two-pass kernel for rows of more than 32 segments (33024 columns).
+NV_SHAPES = [(5, 16), (7, 48), (33, 512), (4, 1008), (3, 1040), (9, 2064), (6, 4096), (3, 5120),
+             (2, 6144), (2, 6160), (5, 7168), (2, 8192), (3, 8208), (2, 12288), (2, 14352),
+             (2, 16400), (1, 24576), (1, 32768), (1, 33024), (2, 3, 256)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])

@@ -18,7 +18,7 @@ def _write_counters(path, counter, rows):
 def test_traffic_is_scaled_by_the_calibration_kernel(tmp_path):
     n = 1 << 30
     neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(x)>(int)"
-    q = "void mxq::k_nvfp4_quant_seg<1, 8, 1, true>(void const*, mxq::NvSegGeom)"
+    q = "void mxq::k_nvfp4_quant_seg<1, 7, 1, true>(void const*, mxq::NvSegGeom)"
     # the fetch counter reads half of the true bytes, the write counter all of them
     _write_counters(tmp_path / "f.csv", "FETCH_SIZE",
                     [(neg, n / 2048), (q, 1000.0), (q, 3000.0)])
