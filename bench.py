@@ -268,7 +268,10 @@ def grouped_gemm(torch, mxq, dev, reps):
     per-expert shapes of the MXFP4 MoE config (32 x [4096, 2048], 512 tokens
     per expert) and the NVFP4 gate/up config (64 x [3072, 4096], 256 tokens
     per expert); synthetic random codes and scales.  Timed with HIP events
-    around `reps` launches each; not part of `value`."""
+    around `reps` launches each; not part of `value`.  For context each entry
+    also times torch.bmm on the same per-expert products with dense bfloat16
+    weights (the vendor BLAS, nothing to dequantize): a practical MFMA rate
+    for these shapes, not a result of this library."""
     g = torch.Generator(device=dev).manual_seed(11)
     out = {"peak_TFLOPs": PEAK_BF16_TFLOPS, "bound": "mfma", "dtype": "bf16"}
     for fmt, E, N, K, per in (("mxfp4", 32, 4096, 2048, 512), ("nvfp4", 64, 3072, 4096, 256)):
@@ -297,9 +300,24 @@ def grouped_gemm(torch, mxq, dev, reps):
             torch.cuda.synchronize()
             t = a.elapsed_time(b) / reps * 1e-3
             tf = 2.0 * T * N * K / t / 1e12
+            # dense reference: [E, per, R] @ [E, R, C], both contiguous
+            xd = x.view(E, per, N if tr else K)
+            wd = torch.randn(E, N if tr else K, K if tr else N, device=dev, generator=g).to(torch.bfloat16)
+            yd = torch.bmm(xd, wd)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(reps):
+                torch.bmm(xd, wd, out=yd)
+            b.record()
+            torch.cuda.synchronize()
+            td = a.elapsed_time(b) / reps * 1e-3
+            tfd = 2.0 * T * N * K / td / 1e12
+            del wd, yd
             out[f"{fmt}_{'backward' if tr else 'forward'}"] = {
                 "experts": E, "N": N, "K": K, "tokens": T, "avg_launch_us": round(t * 1e6, 1),
-                "TFLOPs": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+                "TFLOPs": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "torch_bmm_dense_bf16_TFLOPs": round(tfd, 1),
+                "vs_torch_bmm_dense": round(tf / tfd, 3)}
     return out
 
 
