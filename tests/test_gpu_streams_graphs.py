@@ -21,6 +21,7 @@ def mxq():
 
 def _buffers():
     x = synth.moe_nvfp4((3, 256, 1024), seed=91).to(DEV)
+    x7 = synth.moe_nvfp4((64, 7168), seed=96).to(DEV)    # 7 segments a row: the capped row kernel
     kv = synth.kv_cache((2, 64, 512), seed=92).to(DEV)
     R, K = 3 * 256, 1024
     out = {
@@ -33,6 +34,9 @@ def _buffers():
         "nt_p": torch.empty(3, 256, K // 2, dtype=torch.uint8, device=DEV),
         "nt_s": torch.empty(3, 256, K // 16, dtype=torch.uint8, device=DEV),
         "nt_g": torch.empty(R, dtype=torch.float32, device=DEV),
+        "n7_p": torch.empty(64, 7168 // 2, dtype=torch.uint8, device=DEV),
+        "n7_s": torch.empty(64, 7168 // 16, dtype=torch.uint8, device=DEV),
+        "n7_g": torch.empty(64, dtype=torch.float32, device=DEV),
         "scratch": torch.zeros(4, dtype=torch.float32, device=DEV),
         "kv_y": torch.empty_like(kv),
         "m8_c": torch.empty(3, 256, K, dtype=torch.uint8, device=DEV),
@@ -45,7 +49,7 @@ def _buffers():
         "kq_amax": torch.zeros(8 * 32, dtype=torch.float32, device=DEV),
         "pg_y": torch.empty(64, 8, 128, dtype=torch.bfloat16, device=DEV),
     }
-    return x, kv, out
+    return (x, x7), kv, out
 
 
 def _static_inputs(x):
@@ -64,14 +68,16 @@ def _kv_inputs():
     return k, blocks, (tab(0), tab(1), tab(2))
 
 
-def _sequence(x, kv, o, stream=None, extra=None):
+def _sequence(xs, kv, o, stream=None, extra=None):
     m = mxq()
+    x, x7 = xs
     m.mxq_quantize_mxfp4(x, o["mx_p"], o["mx_s"], stream)
     m.mxq_dequantize_mxfp4(o["mx_p"], o["mx_s"], o["mx_y"], stream)
     m.mxq_quantize_nvfp4(x, o["nv_p"], o["nv_s"], o["nv_g"], stream=stream)
     m.mxq_quantize_nvfp4(x, o["nt_p"], o["nt_s"], o["nt_g"], mode="tensor", scratch=o["scratch"],
                          stream=stream)
     m.mxq_quantize_cache(kv, o["kv_y"], "nvfp4", 16, stream)
+    m.mxq_quantize_nvfp4(x7, o["n7_p"], o["n7_s"], o["n7_g"], stream=stream)
     if extra is not None:
         (a, g), (k, _, (vt, st, at)) = extra
         m.mxq_quantize_mxfp8(x, o["m8_c"], o["m8_s"], stream)
@@ -91,9 +97,9 @@ def _same(a, b):
 
 
 def test_graph_capture_replays_match_eager():
-    x, kv, o = _buffers()
-    extra = (_static_inputs(x), _kv_inputs())
-    _sequence(x, kv, o, extra=extra)
+    xs, kv, o = _buffers()
+    extra = (_static_inputs(xs[0]), _kv_inputs())
+    _sequence(xs, kv, o, extra=extra)
     torch.cuda.synchronize()
     eager = _snapshot(o)
     for v in o.values():
@@ -101,7 +107,7 @@ def test_graph_capture_replays_match_eager():
     s = torch.cuda.Stream()                       # default priority
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        _sequence(x, kv, o, s, extra=extra)
+        _sequence(xs, kv, o, s, extra=extra)
     for replay in range(3):
         for k, v in o.items():
             if k not in ("scratch", "kq_amax"):
@@ -118,20 +124,20 @@ def test_graph_capture_replays_match_eager():
 def test_side_stream_orders_after_producer():
     """A call on a side stream that waits on the producer's event sees the
     producer's data; results equal the default-stream results."""
-    x, kv, o = _buffers()
-    extra = (_static_inputs(x), _kv_inputs())
-    _sequence(x, kv, o, extra=extra)
+    xs, kv, o = _buffers()
+    extra = (_static_inputs(xs[0]), _kv_inputs())
+    _sequence(xs, kv, o, extra=extra)
     torch.cuda.synchronize()
     ref = _snapshot(o)
     s = torch.cuda.Stream()
-    x2 = torch.empty_like(x)
-    x2.copy_(x)                                   # producer on the current stream
+    x2 = torch.empty_like(xs[0])
+    x2.copy_(xs[0])                               # producer on the current stream
     ev = torch.cuda.Event()
     ev.record()
     s.wait_event(ev)
     with torch.cuda.stream(s):
         for v in o.values():
             v.zero_()
-        _sequence(x2, kv, o, s, extra=extra)
+        _sequence((x2, xs[1]), kv, o, s, extra=extra)
     s.synchronize()
     _same(ref, _snapshot(o))
