@@ -302,7 +302,9 @@ def test_nvfp4_sweep_specials():
                 oracle.dequantize_nvfp4(po, so, go, torch.bfloat16), "dequant")
 
 
-@pytest.mark.parametrize("K", [256, 2064])
+# 7168 and 16400 columns take the row kernels with 7 and 5 segments per wave
+# (one and four waves a row), which launch at four workgroups per CU
+@pytest.mark.parametrize("K", [256, 2064, 7168, 16400])
 @pytest.mark.parametrize("kind", ["pow2", "random", "scalar", "edge", "negative", "bounds"])
 def test_nvfp4_given_scales(kind, K):
     say("nvfp4 given", kind, K)
@@ -356,7 +358,7 @@ def test_nvfp4_block_scale_dense_amax():
     assert_same(p, po, "packed")
 
 
-@pytest.mark.parametrize("shape", [(64, 128), (300, 4096), (17, 16)])
+@pytest.mark.parametrize("shape", [(64, 128), (300, 4096), (17, 16), (40, 7168), (6, 16400)])
 def test_nvfp4_tensor_mode(shape):
     say("nvfp4 tensor mode", shape)
     x = synth.moe_nvfp4(shape, seed=shape[0])
