@@ -57,18 +57,21 @@ struct Args {
 };
 
 // Dequantized bf16 of 8 consecutive weights (one packed dword) in the
-// arithmetic of dequantize_mxfp4 / dequantize_nvfp4 with a bf16 output.
+// arithmetic of dequantize_mxfp4 / dequantize_nvfp4 with a bf16 output, up
+// to the sign of zero: code 8 stays -0 here (the dequantizers give +0).  The
+// accumulators start at +0 and +0 + -0 = +0, so no output changes (checked
+// bit for bit against a build that canonicalises), and NVFP4 saves 4 of its
+// 24 VALU operations per 8 weights.
 template <int FMT>
 __device__ __forceinline__ u32x4 deq8(uint32_t w, uint32_t sb, float g) {
-  const uint32_t wc = e2m1_canonical_zeros(w);
   if constexpr (FMT == FMT_MXFP4) {
-    u32x4 o = e2m1_unpack8_bf16_hw(wc, e8m0_as_scale(sb));   // exact
+    u32x4 o = e2m1_unpack8_bf16_hw(w, e8m0_as_scale(sb));   // exact
     if (sb == 255u) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
     return o;
   } else {
     const float sigma = e4m3_decode_any(sb);
     float f[8];
-    e2m1_unpack8_f32_hw(wc, 1.0f, f);
+    e2m1_unpack8_f32_hw(w, 1.0f, f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g;   // exact, then RN
     return u32x4{bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]),

@@ -244,7 +244,8 @@ __device__ __forceinline__ uint32_t e2m1_canonical_zeros(uint32_t w) {
   return w & (nz | 0x77777777u);
 }
 
-// 8 codes -> 8 float32 values e2m1 * scale (exact).  w must be canonical.
+// 8 codes -> 8 float32 values e2m1 * scale (exact).  Code 8 gives -0 unless
+// w is canonical (e2m1_canonical_zeros).
 __device__ __forceinline__ void e2m1_unpack8_f32_hw(uint32_t w, float scale, float out[8]) {
   f32x2 v;
   v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0); out[0] = v.x; out[1] = v.y;
