@@ -265,10 +265,12 @@ __device__ __forceinline__ u32x4 e2m1_unpack8_bf16_hw(uint32_t w, float scale) {
 }
 
 // Two float32 -> packed bfloat16 pair, round to nearest even (v_cvt_pk_bf16_f32,
-// IEEE with subnormals; measured bit-exact).
+// IEEE with subnormals; measured bit-exact).  Written as one vector
+// conversion so that both halves go through a single instruction: two scalar
+// casts compile to one conversion each plus a shift and an OR.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2v));
 }
 
 // ------------------------------------------------------------------ reductions
