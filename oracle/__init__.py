@@ -23,7 +23,7 @@ _SRC = os.path.join(_HERE, "mxq_oracle.c")
 LIB_PATH = os.path.join(_HERE, "liboracle_mxq.so")
 
 CFLAGS = ["-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off",
-          "-fexcess-precision=standard", "-fPIC", "-shared"]
+          "-fexcess-precision=standard", "-fopenmp", "-fPIC", "-shared"]
 
 _DT = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 _FMT = {"fp8": 0, "mxfp4": 1, "nvfp4": 2}
@@ -90,11 +90,25 @@ def lib() -> ctypes.CDLL:
         L.orc_k_smooth_row.argtypes = [vp, i64, i32]
         L.orc_quantize_kv_nvfp4.restype = None
         L.orc_quantize_kv_nvfp4.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp]
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_max_threads.restype = i32
+        L.orc_max_threads.argtypes = []
         L.orc_grouped_mm.restype = None
         L.orc_grouped_mm.argtypes = [vp, i32, i64, vp, i32, i64, i64, i64, vp, i32,
                                      vp, i64, vp, vp]
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's row loops (OpenMP, static schedule over rows;
+    the results do not depend on the count)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ---------------------------------------------------------------- helpers

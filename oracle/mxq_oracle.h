@@ -88,6 +88,10 @@ void orc_grouped_mm(const void* x, int xdt, int64_t T, const void* w, int wdt,
                     int trans, const int64_t* rows, int64_t nrows,
                     double* out, double* absout);
 
+/* Thread count of the OpenMP row loops (results do not depend on it). */
+void orc_set_threads(int n);
+int orc_max_threads(void);
+
 #ifdef __cplusplus
 }
 #endif
