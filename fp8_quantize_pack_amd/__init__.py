@@ -53,7 +53,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build it with "
-            "`python -m fp8_quantize_pack_amd.build` (hipcc, gfx950)")
+            "`python fp8_quantize_pack_amd/build.py` (hipcc, gfx950)")
     L = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.mxq_quantize_mxfp4.argtypes = [vp, i32, i64, i64, vp, vp, vp]
@@ -102,7 +102,12 @@ def _check(status: int, call: str) -> None:
 
 
 def _ptr(t):
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor passed to a C call (host tensors refused)."""
+    if t is None:
+        return None
+    if t.device.type != "cuda" and t.numel():
+        raise ValueError("tensors must live on a GPU")
+    return t.data_ptr()
 
 
 def _stream(t: torch.Tensor, stream=None):
@@ -122,6 +127,20 @@ def _rows(t: torch.Tensor) -> int:
     return t.numel() // k if k else 0
 
 
+def _buf(t, nbytes: int, name: str, call: str, at_least: bool = False) -> None:
+    """A buffer a C call reads or writes must be one contiguous GPU range of
+    exactly the bytes the call touches (at least them, for a scratch word);
+    checked before anything is launched, so a short buffer is an error
+    instead of an access out of bounds."""
+    if t is None:
+        raise ValueError(f"{call}: {name} is required")
+    have = t.numel() * t.element_size()
+    if have < nbytes or (have != nbytes and not at_least):
+        raise ValueError(f"{call}: {name} holds {have} bytes, the call needs {nbytes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{call}: {name} must be contiguous")
+
+
 def _dev_input(t: torch.Tensor) -> torch.Tensor:
     """Contiguous and 16-byte aligned (copies only when it has to)."""
     if t.device.type != "cuda":
@@ -136,6 +155,10 @@ def _dev_input(t: torch.Tensor) -> torch.Tensor:
 
 def mxq_quantize_mxfp4(x, packed, scales, stream=None) -> None:
     K = x.shape[-1]
+    n, c = _rows(x) * K, "mxq_quantize_mxfp4"
+    _buf(x, x.numel() * x.element_size(), "x", c)
+    _buf(packed, n // 2, "packed", c)
+    _buf(scales, n // 32, "scales", c)
     _check(lib.mxq_quantize_mxfp4(_ptr(x), _dt(x.dtype), _rows(x), K,
                                   _ptr(packed), _ptr(scales), _stream(x, stream)),
            "mxq_quantize_mxfp4")
@@ -143,6 +166,10 @@ def mxq_quantize_mxfp4(x, packed, scales, stream=None) -> None:
 
 def mxq_dequantize_mxfp4(packed, scales, y, stream=None) -> None:
     K = y.shape[-1]
+    n, c = _rows(y) * K, "mxq_dequantize_mxfp4"
+    _buf(y, y.numel() * y.element_size(), "y", c)
+    _buf(packed, n // 2, "packed", c)
+    _buf(scales, n // 32, "scales", c)
     _check(lib.mxq_dequantize_mxfp4(_ptr(packed), _ptr(scales), _rows(y), K,
                                     _ptr(y), _dt(y.dtype), _stream(y, stream)),
            "mxq_dequantize_mxfp4")
@@ -151,6 +178,17 @@ def mxq_dequantize_mxfp4(packed, scales, y, stream=None) -> None:
 def mxq_quantize_nvfp4(x, packed, scales, row_scale, mode="row", given=None,
                        given_stride=1, scratch=None, stream=None) -> None:
     K = x.shape[-1]
+    R, c = _rows(x), "mxq_quantize_nvfp4"
+    if mode not in NV_MODES:
+        raise ValueError(f"unknown NVFP4 mode {mode!r}; expected one of {list(NV_MODES)}")
+    _buf(x, x.numel() * x.element_size(), "x", c)
+    _buf(packed, R * K // 2, "packed", c)
+    _buf(scales, R * K // 16, "scales", c)
+    _buf(row_scale, R * 4, "row_scale", c)
+    if mode == "given" and R:
+        _buf(given, 4 * (R if given_stride else 1), "given", c)
+    if mode == "tensor" and R:
+        _buf(scratch, 4, "scratch", c, at_least=True)
     _check(lib.mxq_quantize_nvfp4(_ptr(x), _dt(x.dtype), _rows(x), K,
                                   NV_MODES[mode], _ptr(given), given_stride,
                                   _ptr(scratch), _ptr(packed), _ptr(scales),
@@ -160,6 +198,11 @@ def mxq_quantize_nvfp4(x, packed, scales, row_scale, mode="row", given=None,
 
 def mxq_dequantize_nvfp4(packed, scales, row_scale, y, stream=None) -> None:
     K = y.shape[-1]
+    R, c = _rows(y), "mxq_dequantize_nvfp4"
+    _buf(y, y.numel() * y.element_size(), "y", c)
+    _buf(packed, R * K // 2, "packed", c)
+    _buf(scales, R * K // 16, "scales", c)
+    _buf(row_scale, R * 4, "row_scale", c)
     _check(lib.mxq_dequantize_nvfp4(_ptr(packed), _ptr(scales), _ptr(row_scale),
                                     _rows(y), K, _ptr(y), _dt(y.dtype),
                                     _stream(y, stream)),
@@ -170,12 +213,35 @@ def mxq_quantize_cache(x, y, fmt, block_size, stream=None) -> None:
     if fmt not in FORMATS:
         raise ValueError(f"unknown cache format {fmt!r}; expected one of {list(FORMATS)}")
     C = x.shape[-1] if x.dim() else 1
+    _buf(x, x.numel() * x.element_size(), "x", "mxq_quantize_cache")
+    if y.dtype != x.dtype:
+        raise TypeError("mxq_quantize_cache: y must have x's dtype")
+    _buf(y, x.numel() * x.element_size(), "y", "mxq_quantize_cache")
     _check(lib.mxq_quantize_cache(_ptr(x), _ptr(y), _dt(x.dtype), _rows(x), C,
                                   FORMATS[fmt], int(block_size), _stream(x, stream)),
            "mxq_quantize_cache")
 
 
+def _gemm_bufs(x, packed, scales, offs, y, transpose, block, call) -> None:
+    if x.dim() != 2 or packed.dim() != 3:
+        raise ValueError(f"{call}: x must be [tokens, in_dim] and packed [experts, out_dim, "
+                         "in_dim // 2]")
+    E, N, K = packed.shape[0], packed.shape[1], packed.shape[2] * 2
+    din, dout = (N, K) if transpose else (K, N)
+    if x.shape[1] != din:
+        raise ValueError(f"{call}: x has {x.shape[1]} columns, the weights need {din}")
+    T = x.shape[0]
+    _buf(x, T * din * x.element_size(), "x", call)
+    _buf(packed, E * N * K // 2, "packed", call)
+    _buf(scales, E * N * K // block, "scales", call)
+    _buf(offs, 4 * E, "offs", call)
+    if offs.dtype != torch.int32:
+        raise TypeError(f"{call}: offs must be int32")
+    _buf(y, T * dout * x.element_size(), "y", call)
+
+
 def mxq_grouped_mm_mxfp4(x, packed, scales, offs, y, transpose=False, stream=None) -> None:
+    _gemm_bufs(x, packed, scales, offs, y, transpose, 32, "mxq_grouped_mm_mxfp4")
     E, N, K = packed.shape[0], packed.shape[1], packed.shape[2] * 2
     _check(lib.mxq_grouped_mm_mxfp4(_ptr(x), _dt(x.dtype), x.shape[0], _ptr(packed), _ptr(scales),
                                     E, N, K, _ptr(offs), int(bool(transpose)), _ptr(y),
@@ -185,7 +251,9 @@ def mxq_grouped_mm_mxfp4(x, packed, scales, offs, y, transpose=False, stream=Non
 
 def mxq_grouped_mm_nvfp4(x, packed, scales, row_scale, offs, y, transpose=False,
                          stream=None) -> None:
+    _gemm_bufs(x, packed, scales, offs, y, transpose, 16, "mxq_grouped_mm_nvfp4")
     E, N, K = packed.shape[0], packed.shape[1], packed.shape[2] * 2
+    _buf(row_scale, 4 * E * N, "row_scale", "mxq_grouped_mm_nvfp4")
     _check(lib.mxq_grouped_mm_nvfp4(_ptr(x), _dt(x.dtype), x.shape[0], _ptr(packed), _ptr(scales),
                                     _ptr(row_scale), E, N, K, _ptr(offs), int(bool(transpose)),
                                     _ptr(y), _stream(x, stream)),
@@ -194,6 +262,10 @@ def mxq_grouped_mm_nvfp4(x, packed, scales, row_scale, offs, y, transpose=False,
 
 def mxq_quantize_mxfp8(x, codes, scales, stream=None) -> None:
     K = x.shape[-1]
+    n, c = _rows(x) * K, "mxq_quantize_mxfp8"
+    _buf(x, x.numel() * x.element_size(), "x", c)
+    _buf(codes, n, "codes", c)
+    _buf(scales, n // 32, "scales", c)
     _check(lib.mxq_quantize_mxfp8(_ptr(x), _dt(x.dtype), _rows(x), K, _ptr(codes),
                                   _ptr(scales), _stream(x, stream)),
            "mxq_quantize_mxfp8")
@@ -201,6 +273,10 @@ def mxq_quantize_mxfp8(x, codes, scales, stream=None) -> None:
 
 def mxq_dequantize_mxfp8(codes, scales, y, stream=None) -> None:
     K = y.shape[-1]
+    n, c = _rows(y) * K, "mxq_dequantize_mxfp8"
+    _buf(y, y.numel() * y.element_size(), "y", c)
+    _buf(codes, n, "codes", c)
+    _buf(scales, n // 32, "scales", c)
     _check(lib.mxq_dequantize_mxfp8(_ptr(codes), _ptr(scales), _rows(y), K, _ptr(y),
                                     _dt(y.dtype), _stream(y, stream)),
            "mxq_dequantize_mxfp8")
@@ -209,6 +285,15 @@ def mxq_dequantize_mxfp8(codes, scales, y, stream=None) -> None:
 def mxq_fake_quantize_fp4_static(x, block_amax, global_amax, y, block_size,
                                  stream=None) -> None:
     K = x.shape[-1]
+    n, c = _rows(x) * K, "mxq_fake_quantize_fp4_static"
+    _buf(x, x.numel() * x.element_size(), "x", c)
+    if y.dtype != x.dtype:
+        raise TypeError(f"{c}: y must have x's dtype")
+    _buf(y, x.numel() * x.element_size(), "y", c)
+    if block_size >= 1 and K % block_size == 0:
+        _buf(block_amax, 4 * (n // block_size), "block_amax", c)
+    if n:
+        _buf(global_amax, 4, "global_amax", c)
     _check(lib.mxq_fake_quantize_fp4_static(_ptr(x), _dt(x.dtype), _rows(x), K,
                                             int(block_size), _ptr(block_amax),
                                             _ptr(global_amax), _ptr(y), _stream(x, stream)),
@@ -222,6 +307,11 @@ def mxq_dequantize_kv_pages_nvfp4(values_ptrs, scales_ptrs, amax_ptrs, block_tok
     (a leading batch dim of 1 is allowed)."""
     H, D = y.shape[-2], y.shape[-1]
     nb = values_ptrs.numel()
+    c = "mxq_dequantize_kv_pages_nvfp4"
+    for t, name in ((values_ptrs, "values_ptrs"), (scales_ptrs, "scales_ptrs"),
+                    (amax_ptrs, "amax_ptrs")):
+        _buf(t, 8 * nb, name, c)
+    _buf(y, nb * int(block_tokens) * H * D * y.element_size(), "y", c)
     _check(lib.mxq_dequantize_kv_pages_nvfp4(_ptr(values_ptrs), _ptr(scales_ptrs), _ptr(amax_ptrs),
                                              nb, int(block_tokens), H, D, _ptr(y), _dt(y.dtype),
                                              _stream(y, stream)),
@@ -231,6 +321,13 @@ def mxq_dequantize_kv_pages_nvfp4(values_ptrs, scales_ptrs, amax_ptrs, block_tok
 def mxq_quantize_kv_nvfp4(k, head_amax, packed, scales, row_scale, smooth=True,
                           stream=None) -> None:
     S, H, D = k.shape[-3], k.shape[-2], k.shape[-1]
+    S = k.numel() // (H * D) if k.numel() else 0
+    c = "mxq_quantize_kv_nvfp4"
+    _buf(k, k.numel() * k.element_size(), "k", c)
+    _buf(head_amax, 4 * H * KV_AMAX_SLOTS, "head_amax", c)
+    _buf(packed, S * H * D // 2, "packed", c)
+    _buf(scales, S * H * D // 16, "scales", c)
+    _buf(row_scale, 4 * S * H, "row_scale", c)
     _check(lib.mxq_quantize_kv_nvfp4(_ptr(k), _dt(k.dtype), S, H, D, int(bool(smooth)),
                                      _ptr(head_amax), _ptr(packed), _ptr(scales),
                                      _ptr(row_scale), _stream(k, stream)),
@@ -255,11 +352,12 @@ def quantize_mxfp4(weight: torch.Tensor):
 def dequantize_mxfp4(packed: torch.Tensor, scales: torch.Tensor,
                      dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     """(int8 [..., K//2], e8m0 [..., K//32]) -> [..., K] in dtype."""
+    K = packed.shape[-1] * 2
+    if (K % MXFP4_BLOCK_SIZE
+            or tuple(scales.shape) != (*packed.shape[:-1], K // MXFP4_BLOCK_SIZE)):
+        raise ValueError("packed/scales shapes do not describe 32-column blocks")
     p = _dev_input(packed.view(torch.int8))
     s = _dev_input(scales.view(torch.uint8))
-    K = p.shape[-1] * 2
-    if K % MXFP4_BLOCK_SIZE or s.shape[-1] != K // MXFP4_BLOCK_SIZE:
-        raise ValueError("packed/scales shapes do not describe 32-column blocks")
     y = torch.empty(*p.shape[:-1], K, dtype=dtype, device=p.device)
     mxq_dequantize_mxfp4(p, s, y)
     return y
@@ -316,12 +414,16 @@ def dequantize_nvfp4(packed: torch.Tensor, scales: torch.Tensor,
                      global_scale: torch.Tensor,
                      dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     """(uint8/int8 [..., K//2], e4m3 [..., K//16], float32 [...]) -> [..., K]."""
+    K = packed.shape[-1] * 2
+    _check_last_dim(K)
+    if tuple(scales.shape) != (*packed.shape[:-1], K // NVFP4_BLOCK_SIZE):
+        raise ValueError("scales do not describe 16-column blocks of packed")
+    try:
+        torch.broadcast_shapes(tuple(global_scale.shape), tuple(packed.shape[:-1]))
+    except RuntimeError:
+        raise ValueError("global_scale does not broadcast to one value per row") from None
     p = _dev_input(packed.view(torch.uint8))
     s = _dev_input(scales.view(torch.uint8))
-    K = p.shape[-1] * 2
-    _check_last_dim(K)
-    if s.shape[-1] != K // NVFP4_BLOCK_SIZE:
-        raise ValueError("scales do not describe 16-column blocks of packed")
     g = global_scale.to(device=p.device, dtype=torch.float32)
     g = g.expand(p.shape[:-1]).contiguous()
     y = torch.empty(*p.shape[:-1], K, dtype=dtype, device=p.device)
@@ -345,9 +447,19 @@ def quantize_cache(values: torch.Tensor, format: str, block_size: int) -> torch.
     return y
 
 
-def _grouped_mm_out(x: torch.Tensor, packed: torch.Tensor, transpose: bool) -> torch.Tensor:
+def _grouped_mm_shapes(x, packed, scales, offs, block, row_scale=None) -> None:
     if x.dim() != 2 or packed.dim() != 3:
         raise ValueError("x must be [tokens, in_dim] and packed [experts, out_dim, in_dim // 2]")
+    E, N, K = packed.shape[0], packed.shape[1], packed.shape[2] * 2
+    if tuple(scales.shape) != (E, N, K // block):
+        raise ValueError(f"scales must be [{E}, {N}, {K // block}], got {list(scales.shape)}")
+    if row_scale is not None and tuple(row_scale.shape) != (E, N):
+        raise ValueError(f"row_scale must be [{E}, {N}], got {list(row_scale.shape)}")
+    if offs.numel() != E:
+        raise ValueError(f"offs must hold one count per expert ({E}), got {offs.numel()}")
+
+
+def _grouped_mm_out(x: torch.Tensor, packed: torch.Tensor, transpose: bool) -> torch.Tensor:
     N, K = packed.shape[1], packed.shape[2] * 2
     din, dout = (N, K) if transpose else (K, N)
     if x.shape[1] != din:
@@ -360,8 +472,9 @@ def grouped_mm_mxfp4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
     """Grouped GEMM over MXFP4 expert weights ([mxfp4 page] MXFP4GroupedMM):
     x [tokens, K] grouped by expert (offs: int32 cumulative counts), packed
     [E, N, K // 2], scales [E, N, K // 32]; returns x @ W_e^T [tokens, N], or
-    with transpose=True x [tokens, N] @ W_e [tokens, K] (the backward product).
+    with transpose=True x [tokens, N] @ W_e, [tokens, K] (the backward product).
     Rows outside every group are left uninitialised."""
+    _grouped_mm_shapes(x, packed, scales, offs, MXFP4_BLOCK_SIZE)
     x, packed, scales = _dev_input(x), _dev_input(packed), _dev_input(scales)
     offs = _dev_input(offs.to(torch.int32))
     y = _grouped_mm_out(x, packed, transpose)
@@ -375,6 +488,7 @@ def grouped_mm_nvfp4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor
     """Grouped GEMM over NVFP4 expert weights ([nvfp4 page] NVFP4GroupedMM):
     as grouped_mm_mxfp4, with e4m3 scales [E, N, K // 16] and float32
     row_scale [E, N]."""
+    _grouped_mm_shapes(x, packed, scales, offs, NVFP4_BLOCK_SIZE, row_scale)
     x, packed, scales = _dev_input(x), _dev_input(packed), _dev_input(scales)
     row_scale = _dev_input(row_scale.to(torch.float32))
     offs = _dev_input(offs.to(torch.int32))
@@ -406,7 +520,8 @@ def dequantize_mxfp8(codes: torch.Tensor, scales: torch.Tensor,
                      dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     """(e4m3 [..., K], e8m0 [..., K//32]) -> [..., K] in dtype."""
     K = codes.shape[-1]
-    if K % MXFP8_BLOCK_SIZE or scales.shape[-1] != K // MXFP8_BLOCK_SIZE:
+    if (K % MXFP8_BLOCK_SIZE
+            or tuple(scales.shape) != (*codes.shape[:-1], K // MXFP8_BLOCK_SIZE)):
         raise ValueError("codes/scales shapes do not describe 32-column blocks")
     c = _dev_input(codes.view(torch.uint8))
     s = _dev_input(scales.view(torch.uint8))
@@ -482,15 +597,11 @@ def quantize_kv_nvfp4(k: torch.Tensor, smooth: bool = True):
         raise ValueError("head_dim must be a power of two in [16, 512]")
     x = _dev_input(k)
     lead = tuple(x.shape[:-1])
-    S = x.numel() // (x.shape[-2] * D) if x.numel() else 0
     packed = torch.empty(*lead, D // 2, dtype=torch.uint8, device=x.device)
     scales = torch.empty(*lead, D // 16, dtype=torch.uint8, device=x.device)
     row_scale = torch.empty(lead, dtype=torch.float32, device=x.device)
     head_amax = torch.empty(x.shape[-2] * KV_AMAX_SLOTS, dtype=torch.float32, device=x.device)
-    _check(lib.mxq_quantize_kv_nvfp4(_ptr(x), _dt(x.dtype), S, x.shape[-2], D, int(bool(smooth)),
-                                     _ptr(head_amax), _ptr(packed), _ptr(scales),
-                                     _ptr(row_scale), _stream(x)),
-           "mxq_quantize_kv_nvfp4")
+    mxq_quantize_kv_nvfp4(x, head_amax, packed, scales, row_scale, smooth)
     return packed, scales.view(torch.float8_e4m3fn), row_scale
 
 

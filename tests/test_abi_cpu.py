@@ -201,3 +201,83 @@ def test_python_wrappers_of_the_newer_calls_check_their_arguments():
     with pytest.raises(ValueError, match="GPU"):
         mxq.quantize_mxfp8(torch.zeros(2, 64))
 
+
+
+def test_tensor_api_rejects_mismatched_scale_and_offs_shapes():
+    """Short scale arrays, row scales or offs would make a kernel read past
+    its allocation; the binding rejects them before anything is launched."""
+    import torch
+    import fp8_quantize_pack_amd as mxq
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="32-column blocks"):
+        mxq.dequantize_mxfp4(u8(8, 32), u8(4, 2))             # fewer scale rows
+    with pytest.raises(ValueError, match="32-column blocks"):
+        mxq.dequantize_mxfp4(u8(2, 4, 32), u8(8, 2))          # same numel, other shape
+    with pytest.raises(ValueError, match="16-column blocks"):
+        mxq.dequantize_nvfp4(u8(8, 32), u8(7, 4), torch.ones(8))
+    with pytest.raises(ValueError, match="one value per row"):
+        mxq.dequantize_nvfp4(u8(8, 32), u8(8, 4), torch.ones(5))
+    with pytest.raises(ValueError, match="32-column blocks"):
+        mxq.dequantize_mxfp8(u8(8, 64), u8(3, 2))
+    x = torch.zeros(64, 256, dtype=torch.bfloat16)
+    pk = u8(4, 128, 128)                                      # E=4, N=128, K=256
+    offs = torch.full((4,), 64, dtype=torch.int32)
+    with pytest.raises(ValueError, match="scales must be"):
+        mxq.grouped_mm_mxfp4(x, pk, u8(4, 128, 4), offs)
+    with pytest.raises(ValueError, match="one count per expert"):
+        mxq.grouped_mm_mxfp4(x, pk, u8(4, 128, 8), offs[:3])
+    with pytest.raises(ValueError, match="scales must be"):
+        mxq.grouped_mm_nvfp4(x, pk, u8(4, 128, 8), torch.ones(4, 128), offs)
+    with pytest.raises(ValueError, match="row_scale must be"):
+        mxq.grouped_mm_nvfp4(x, pk, u8(4, 128, 16), torch.ones(4, 64), offs)
+    with pytest.raises(ValueError, match="one count per expert"):
+        mxq.grouped_mm_nvfp4(x, pk, u8(4, 128, 16), torch.ones(4, 128), offs[:2])
+
+
+def test_c_abi_wrappers_check_every_buffer_size():
+    """The one-to-one wrappers compute the byte count each buffer must hold
+    and reject a short or long one before the call (so a caller-allocated
+    output that is too small never reaches a kernel)."""
+    import torch
+    import fp8_quantize_pack_amd as mxq
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)
+    x = torch.zeros(8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="packed holds 255 bytes"):
+        mxq.mxq_quantize_mxfp4(x, u8(255), u8(16))
+    with pytest.raises(ValueError, match="scales holds"):
+        mxq.mxq_quantize_mxfp4(x, u8(256), u8(15))
+    with pytest.raises(ValueError, match="row_scale holds"):
+        mxq.mxq_quantize_nvfp4(x, u8(256), u8(32), torch.zeros(7))
+    with pytest.raises(ValueError, match="given holds"):
+        mxq.mxq_quantize_nvfp4(x, u8(256), u8(32), torch.zeros(8), mode="given",
+                               given=torch.ones(4), given_stride=1)
+    with pytest.raises(ValueError, match="scratch is required"):
+        mxq.mxq_quantize_nvfp4(x, u8(256), u8(32), torch.zeros(8), mode="tensor")
+    with pytest.raises(ValueError, match="unknown NVFP4 mode"):
+        mxq.mxq_quantize_nvfp4(x, u8(256), u8(32), torch.zeros(8), mode="col")
+    with pytest.raises(ValueError, match="scales holds"):
+        mxq.mxq_dequantize_nvfp4(u8(256), u8(31), torch.zeros(8), x)
+    with pytest.raises(ValueError, match="y holds"):
+        mxq.mxq_quantize_cache(x, torch.zeros(8, 63, dtype=torch.bfloat16), "fp8", 32)
+    with pytest.raises(TypeError, match="x's dtype"):
+        mxq.mxq_quantize_cache(x, torch.zeros(8, 64), "fp8", 32)
+    with pytest.raises(ValueError, match="codes holds"):
+        mxq.mxq_quantize_mxfp8(x, u8(511), u8(16))
+    with pytest.raises(ValueError, match="block_amax holds"):
+        mxq.mxq_fake_quantize_fp4_static(x, torch.zeros(31), torch.ones(1), x.clone(), 16)
+    with pytest.raises(ValueError, match="head_amax holds"):
+        mxq.mxq_quantize_kv_nvfp4(torch.zeros(4, 2, 64, dtype=torch.bfloat16), torch.zeros(63),
+                                  u8(256), u8(32), torch.zeros(8))
+    with pytest.raises(ValueError, match="must be contiguous"):
+        mxq.mxq_quantize_mxfp4(x, u8(512)[::2], u8(16))
+    with pytest.raises(ValueError, match="GPU"):
+        mxq.mxq_quantize_mxfp4(x, u8(256), u8(16))
+    pk = u8(4, 128, 128)
+    with pytest.raises(ValueError, match="offs holds"):
+        mxq.mxq_grouped_mm_mxfp4(torch.zeros(64, 256, dtype=torch.bfloat16), pk, u8(4, 128, 8),
+                                 torch.zeros(3, dtype=torch.int32),
+                                 torch.zeros(64, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="y holds"):
+        mxq.mxq_grouped_mm_nvfp4(torch.zeros(64, 256, dtype=torch.bfloat16), pk, u8(4, 128, 16),
+                                 torch.ones(4, 128), torch.zeros(4, dtype=torch.int32),
+                                 torch.zeros(64, 256, dtype=torch.bfloat16))
