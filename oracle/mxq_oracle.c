@@ -105,6 +105,32 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------
+ * Threads.  The row loops below are OpenMP loops with a static schedule:
+ * rows are independent and each row's arithmetic runs on one thread in the
+ * order written, so the results do not depend on the thread count.  The
+ * count is the oracle's own (set by orc_set_threads, else the runtime's
+ * default) and is passed to every loop, so that other users of the same
+ * OpenMP runtime in the process cannot change it.
+ * ---------------------------------------------------------------------- */
+static int g_threads = 0;
+
+static int team(void) {
+#ifdef _OPENMP
+  return g_threads > 0 ? g_threads : omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void orc_set_threads(int n) { g_threads = n > 0 ? n : 0; }
+
+int orc_max_threads(void) { return team(); }
+
 /* ------------------------------------------------------------------------
  * Number formats
  * ---------------------------------------------------------------------- */
@@ -283,7 +309,7 @@ void orc_store(void* y, int dtype, int64_t i, float v) {
 void orc_quantize_mxfp4(const void* x, int dtype, int64_t rows, int64_t K,
                         uint8_t* packed, uint8_t* scales) {
   int64_t nblk = K / MXFP4_BLOCK;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t b = 0; b < nblk; ++b) {
       int64_t base = r * K + b * MXFP4_BLOCK;
@@ -317,7 +343,7 @@ void orc_quantize_mxfp4(const void* x, int dtype, int64_t rows, int64_t K,
 void orc_dequantize_mxfp4(const uint8_t* packed, const uint8_t* scales,
                           int64_t rows, int64_t K, void* y, int dtype) {
   int64_t nblk = K / MXFP4_BLOCK;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t k = 0; k < K; ++k) {
       int64_t i = r * K + k;
@@ -358,13 +384,13 @@ void orc_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t K,
   int64_t nblk = K / NVFP4_BLOCK;
   float tensor_amax = 0.0f;
   if (mode == 2) {
-#pragma omp parallel for schedule(static) reduction(max : tensor_amax)
+#pragma omp parallel for schedule(static) num_threads(team()) reduction(max : tensor_amax)
     for (int64_t i = 0; i < rows * K; ++i) {
       float v = fabsf(orc_load(x, dtype, i));
       if (v > tensor_amax) tensor_amax = v;
     }
   }
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t r = 0; r < rows; ++r) {
     /* step 1: the row's global scale */
     float g;
@@ -415,7 +441,7 @@ void orc_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales,
                           const float* row_scale, int64_t rows, int64_t K,
                           void* y, int dtype) {
   int64_t nblk = K / NVFP4_BLOCK;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t r = 0; r < rows; ++r) {
     float g = row_scale[r];
     for (int64_t k = 0; k < K; ++k) {
@@ -480,7 +506,7 @@ static void cache_group(const void* x, void* y, int dtype, int64_t base,
 
 void orc_quantize_cache(const void* x, void* y, int dtype, int64_t rows,
                         int64_t C, int fmt, int64_t block_size) {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t c0 = 0; c0 < C; c0 += block_size) {
       int64_t n = (C - c0 < block_size) ? C - c0 : block_size;
@@ -502,7 +528,7 @@ void orc_grouped_mm(const void* x, int xdt, int64_t T, const void* w, int wdt,
                     int trans, const int64_t* rows, int64_t nrows,
                     double* out, double* absout) {
   int64_t din = trans ? N : K, dout = trans ? K : N;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t i = 0; i < nrows; ++i) {
     int64_t r = rows[i];
     int64_t e = -1, lo = 0;
@@ -539,7 +565,7 @@ void orc_grouped_mm(const void* x, int xdt, int64_t T, const void* w, int wdt,
 void orc_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_t K,
                         uint8_t* codes, uint8_t* scales) {
   int64_t nblk = K / MXFP8_BLOCK;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t b = 0; b < nblk; ++b) {
       int64_t base = r * K + b * MXFP8_BLOCK;
@@ -566,7 +592,7 @@ void orc_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_t K,
 void orc_dequantize_mxfp8(const uint8_t* codes, const uint8_t* scales,
                           int64_t rows, int64_t K, void* y, int dtype) {
   int64_t nblk = K / MXFP8_BLOCK;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t k = 0; k < K; ++k) {
       int64_t i = r * K + k;
@@ -608,7 +634,7 @@ void orc_fake_quantize_fp4_static(const void* x, int dtype, int64_t rows,
                                   int64_t K, int64_t block,
                                   const float* block_amax, float G, void* y) {
   int64_t nblk = K / block;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t b = 0; b < nblk; ++b) {
       float sp = orc_static_block_scale(block_amax[r * nblk + b], G);
@@ -639,7 +665,7 @@ void orc_dequantize_kv_pages(const uint8_t* const* values,
   int64_t rows = block_tokens * H;
   for (int64_t b = 0; b < nblocks; ++b) {
     float g = amax[b] / (E2M1_MAX * E4M3_MAX);
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
     for (int64_t r = 0; r < rows; ++r) {
       for (int64_t d = 0; d < D; ++d) {
         uint8_t byte = values[b][(r * D + d) / 2];
@@ -692,7 +718,7 @@ void orc_quantize_kv_nvfp4(const void* k, int dtype, int64_t S, int64_t H,
   float* g = (float*)malloc(sizeof(float) * (size_t)S);
   for (int64_t h = 0; h < H; ++h) {
     /* the head's slice k[:, h, :], smoothed row by row */
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(team())
     for (int64_t s = 0; s < S; ++s) {
       for (int64_t d = 0; d < D; ++d)
         slice[s * D + d] = orc_load(k, dtype, (s * H + h) * D + d);
@@ -713,29 +739,4 @@ void orc_quantize_kv_nvfp4(const void* k, int dtype, int64_t S, int64_t H,
   free(p);
   free(sc);
   free(g);
-}
-
-/* ------------------------------------------------------------------------
- * Threads.  The row loops above are OpenMP loops with a static schedule:
- * rows are independent and each row's arithmetic runs on one thread in the
- * order written, so the results do not depend on the thread count.
- * ---------------------------------------------------------------------- */
-#ifdef _OPENMP
-#include <omp.h>
-#endif
-
-void orc_set_threads(int n) {
-#ifdef _OPENMP
-  if (n > 0) omp_set_num_threads(n);
-#else
-  (void)n;
-#endif
-}
-
-int orc_max_threads(void) {
-#ifdef _OPENMP
-  return omp_get_max_threads();
-#else
-  return 1;
-#endif
 }
