@@ -53,9 +53,11 @@ struct NvSegGeom {
   int nseg;         // 64-block segments per row = ceil(bpr / 64)
 };
 
-// One segment's two chunks of this lane (zero outside the row).
+// One segment's two chunks of this lane (zero outside the row) and their
+// magnitude maxima as ordered bit patterns (amax8_bits), taken once: the row
+// maximum and the block maxima both use them.
 template <int DT>
-struct SegChunks { Raw8<DT> c0, c1; };
+struct SegChunks { Raw8<DT> c0, c1; uint32_t m0, m1; };
 
 // With FULL (every segment of a row has 64 blocks) the guards depend only on
 // the row and the segment, which are uniform over the wave.
@@ -68,6 +70,8 @@ __device__ __forceinline__ SegChunks<DT> seg_load(const void* x, const NvSegGeom
   SegChunks<DT> c;
   c.c0 = ok0 ? ld8<DT>(x, cbase + ch0) : zero8<DT>();
   c.c1 = ok1 ? ld8<DT>(x, cbase + ch0 + 64) : zero8<DT>();
+  c.m0 = amax8_bits<DT>(c.c0);
+  c.m1 = amax8_bits<DT>(c.c1);
   return c;
 }
 
@@ -78,17 +82,15 @@ __device__ __forceinline__ void seg_quant(const SegChunks<DT>& c, const NvSegGeo
                                           bool row_ok, int64_t row, int seg, int lane,
                                           float g, double rg, uint32_t* __restrict__ packed,
                                           uint8_t* __restrict__ scales) {
-  uint32_t p0 = amax8_bits<DT>(c.c0), p1 = amax8_bits<DT>(c.c1);
-  p0 = max(p0, pair_swap(p0));                          // block of chunk 0
-  p1 = max(p1, pair_swap(p1));                          // block of chunk 1
+  const uint32_t p0 = max(c.m0, pair_swap(c.m0));      // block of chunk 0
+  const uint32_t p1 = max(c.m1, pair_swap(c.m1));      // block of chunk 1
   const bool odd = lane & 1;
   uint32_t sb;
   const float a = amax_from_bits<DT>(odd ? p1 : p0);
   const double mine = NORMAL ? nv_block_recip_normal(a, g, rg, sb) : nv_block_recip(a, g, rg, sb);
   const double other = pair_swap(mine);
-  const double r0 = odd ? other : mine, r1 = odd ? mine : other;
-  const uint32_t w0 = nv_codes8<DT>(c.c0, r0);
-  const uint32_t w1 = nv_codes8<DT>(c.c1, r1);
+  const uint32_t w0 = nv_codes8<DT>(c.c0, odd ? other : mine);
+  const uint32_t w1 = nv_codes8<DT>(c.c1, odd ? mine : other);
   const int64_t ch0 = (int64_t)seg * 128 + lane;
   const int64_t cbase = row * geo.cpr;
   const int64_t blk = (int64_t)seg * 64 + (odd ? 32 : 0) + (lane >> 1);
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_seg(
       if (mode == 0) {
         uint32_t m = 0;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) m = max(m, max(amax8_bits<DT>(c[it].c0), amax8_bits<DT>(c[it].c1)));
+        for (int it = 0; it < NIT; ++it) m = max(m, max(c[it].m0, c[it].m1));
         amax = amax_from_bits<DT>(m);
       }
     } else {
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_seg(
         uint32_t m = 0;
         for (int seg = wir; seg < geo.nseg; seg += WPR) {
           const SegChunks<DT> t = seg_load<DT, FULL>(x, geo, row_ok, cbase, seg, lane);
-          m = max(m, max(amax8_bits<DT>(t.c0), amax8_bits<DT>(t.c1)));
+          m = max(m, max(t.m0, t.m1));
         }
         amax = amax_from_bits<DT>(m);
       }

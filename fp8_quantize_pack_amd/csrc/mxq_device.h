@@ -227,18 +227,16 @@ MXQ_HD float f16_to_f32(uint32_t h) {
 
 // ---------------------------------------------------------------- exact NVFP4 helpers
 
-// float32 round-to-nearest of a / 6 (a >= 0 finite).  Computed as a binary64
-// product with a correctly rounded 1/6, then one rounding to float32.  This
-// equals the correctly rounded float32 quotient whenever that quotient is a
-// normal number: a / 6 is never a float32 half-way point (its odd part is not
-// dyadic unless 3 divides a's significand, in which case the quotient is
-// exact), its relative distance to the nearest half-way point is at least
-// 2^-27, and the binary64 error is below 2^-52.  Subnormal quotients (a below
-// 6 * 2^-126) use a true division.
-MXQ_HD float div6_rn(float a) {
-  if (a < 8.0e-38f) return a / 6.0f;   // 6 * 2^-126 ~= 7.05e-38
-  return (float)((double)a * (1.0 / 6.0));
-}
+// float32 round-to-nearest of a / 6 (a >= 0 finite), as a binary64 product
+// with a correctly rounded 1/6, rounded once to float32.  This equals the
+// correctly rounded float32 quotient, subnormal results included: a / 6 =
+// (a / 2) / 3 is either exact (when 3 divides a's significand) or not dyadic,
+// so it is never a float32 rounding boundary.  For a normal quotient its
+// relative distance to the nearest boundary is at least 2^-27; for a
+// subnormal one (a below 6 * 2^-126) a and every boundary are multiples of
+// 2^-150, so the distance is at least 2^-150 / 6.  The binary64 product is
+// within 2^-52 (relative) of a / 6: far closer than either margin.
+MXQ_HD float div6_rn(float a) { return (float)((double)a * (1.0 / 6.0)); }
 
 // ---------------------------------------------------------------- per-chunk steps
 // The kernels hand 8 consecutive elements (one "chunk", already widened to
