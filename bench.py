@@ -15,10 +15,15 @@ timed steps replay the step's launches captured once as a HIP graph (the same
 kernels with the same arguments, without host launch gaps between them);
 `--eager` times eager launches instead, and `eager_GBps` always reports them.
 
-Prints one JSON line.  Also reports, per kernel, its average launch duration
-from HIP events recorded on the launch stream (eager launches), the roofline of
-the dominant kernel against MI355X's 8 TB/s HBM peak, and the CPU oracle timed
-on a bounded sample of the same workload.
+Prints one JSON line.  Also reports, per operation, its average launch
+duration from a HIP graph of its launches replayed back to back (the sweep's
+eight chunk launches; eight rotating buffer sets for the cache round trips, so
+that no launch finds its input in the 256 MB last-level cache), timed with HIP
+events on the launch stream; the roofline of the dominant kernel against
+MI355X's 8 TB/s HBM peak and against a plain copy of the same size (the
+practical ceiling, from the reference kernels of libmxq_roofline); and the CPU
+oracle timed on a bounded sample of the same workload, on one thread and on all
+the host's threads.
 """
 from __future__ import annotations
 
@@ -54,8 +59,10 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time the steps as eager launches instead of HIP graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after the timed steps, run a torch negation over one 36-expert chunk "
-                         "(reads and writes CALIBRATION_BYTES) for HBM counter calibration")
+                    help="after the timed steps, run the reference copy kernel over one 36-expert "
+                         "chunk (reads and writes CALIBRATION_BYTES) for HBM counter calibration")
+    ap.add_argument("--no-ref", action="store_true",
+                    help="skip the copy / read / write reference kernels")
     return ap.parse_args()
 
 
@@ -190,32 +197,71 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
 
-    # per-kernel averages from the events
-    ops = {}
-    for s in range(args.steps):
+    # per-launch durations from HIP event pairs around every eager launch
+    ev_ops = {}
+    for st in range(args.steps):
         for i, (name, b, _) in enumerate(plan):
-            t = ev[s][i][0].elapsed_time(ev[s][i][1])
-            o = ops.setdefault(name, {"launches": 0, "bytes": 0, "ms": 0.0})
-            o["launches"] += 1; o["bytes"] += b; o["ms"] += t
-    for name, o in ops.items():
-        o["avg_launch_us"] = round(o["ms"] * 1e3 / o["launches"], 2)
-        o["GBps"] = round(o["bytes"] / (o["ms"] * 1e-3) / 1e9, 1)
-        o["frac_of_peak"] = round(o["GBps"] / PEAK_HBM_GBPS, 4)
-        o["ms"] = round(o["ms"], 3)
+            o = ev_ops.setdefault(name, [0, 0.0])
+            o[0] += 1
+            o[1] += ev[st][i][0].elapsed_time(ev[st][i][1])
+
+    # per-operation durations from graphs of back-to-back launches: the
+    # sweep's chunk launches of one operation, or the cache round trip over
+    # CACHE_SETS rotating buffer sets (the sets of one case together exceed
+    # the 256 MB last-level cache, so every launch reads cold input, as in the
+    # step, where 7 GB of sweep traffic runs between two uses)
+    cache_sets = {c: [(cache_in[c], cache_out[c])] + [
+        (synth.kv_cache(synth.SHAPES[c], seed=synth.SEEDS[c] * 100 + i, device=dev),
+         torch.empty_like(cache_in[c])) for i in range(1, CACHE_SETS)] for c, _, _ in cache_cases}
+    op_launches = {}
+    for name, b, fn in plan:
+        if not name.startswith("cache"):
+            op_launches.setdefault(name, []).append((b, fn))
+    for c, fmt, B in cache_cases:
+        op_launches[f"cache_{fmt}"] = [
+            (4 * xi.numel(), lambda xi=xi, yo=yo, fmt=fmt, B=B: mxq.mxq_quantize_cache(xi, yo, fmt, B))
+            for _ in range(CACHE_CYCLES) for xi, yo in cache_sets[c]]
+    reps = max(args.steps, 5)
+    ops = {}
+    op_times = time_graphs_interleaved(torch, {n: [fn for _, fn in l] for n, l in op_launches.items()},
+                                       reps)
+    for name, launches in op_launches.items():
+        t = op_times[name]
+        nb = sum(b for b, _ in launches)
+        n_ev, ms_ev = ev_ops[name]
+        per_step_launches = sum(1 for n, _, _ in plan if n == name)
+        ops[name] = {"launches_per_graph": len(launches), "graph_replays": reps,
+                     "bytes_per_launch": nb // len(launches),
+                     "avg_launch_us": round(t / len(launches) * 1e6, 2),
+                     "GBps": round(nb / t / 1e9, 1), "frac_of_peak": round(nb / t / 1e9 / PEAK_HBM_GBPS, 4),
+                     "event_pair_avg_us": round(ms_ev * 1e3 / n_ev, 2),
+                     "step_us": round(t / len(launches) * per_step_launches * 1e6, 1)}
+    del cache_sets
+    progress("per-operation graphs timed")
     fp4 = [n for n in ops if not n.startswith("cache")]
-    fp4_bytes = sum(ops[n]["bytes"] for n in fp4)
-    fp4_ms = sum(ops[n]["ms"] for n in fp4)
-    dom = max(ops, key=lambda n: ops[n]["ms"])
+    fp4_bytes = sum(b for n, b, _ in plan if n in fp4)
+    fp4_s = sum(ops[n]["step_us"] for n in fp4) * 1e-6
+    dom = max(ops, key=lambda n: ops[n]["step_us"])
     src_hash = kernel_source_hash()
-    for o in ops.values():
-        o["bytes_per_launch"] = o["bytes"] // o["launches"]
     traffic = measured_traffic(dom, src_hash)
+
+    ref = None if args.no_ref else reference_rates(torch, dev, x, y, reps)
+    progress("reference copy / read / write measured" if ref else "reference kernels skipped")
     achieved = ops[dom]["GBps"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic,
-                "algorithmic_bytes_per_launch": ops[dom]["bytes"] // ops[dom]["launches"],
+                "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"],
                 "avg_launch_us": ops[dom]["avg_launch_us"]}
+    if ref:
+        cp = ref["copy"]["sweep_chunk"]
+        roofline["copy_GBps"] = cp["GBps"]
+        roofline["copy_bytes_per_launch"] = cp["bytes_per_launch"]
+        roofline["frac_of_copy"] = round(achieved / cp["GBps"], 4)
+        for n, o in ops.items():
+            size = "sweep_chunk" if not n.startswith("cache") else (
+                "cache_256MiB" if n == "cache_fp8" else "cache_64MiB")
+            o["frac_of_same_size_copy"] = round(o["GBps"] / ref["copy"][size]["GBps"], 4)
 
     gemm = None if args.no_gemm else grouped_gemm(torch, mxq, dev, max(args.steps, 1))
     progress("grouped GEMM measured" if gemm else "grouped GEMM skipped")
@@ -223,11 +269,12 @@ def main():
     progress("extra ops measured" if extra else "extra ops skipped")
 
     if args.calibrate_copy:
-        # a plain elementwise kernel of known traffic, outside the timed region
+        # a plain copy kernel of known traffic, outside the timed region
+        from fp8_quantize_pack_amd import roofline as rl
         xs, ys = x[:synth.C5_CHUNK_EXPERTS], y[:synth.C5_CHUNK_EXPERTS]
         assert xs.numel() * xs.element_size() == CALIBRATION_BYTES
         for _ in range(3):
-            torch.neg(xs, out=ys)
+            rl.copy(xs, ys, unroll=2)
         torch.cuda.synchronize()
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
@@ -240,7 +287,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "MoE expert sweep bf16 [%d,2048,7168] in 36-expert chunks: MXFP4 + NVFP4 "
                                "quantize-pack and dequantize to bf16; plus cache QDQ fp8/b32 [16,8192,512], "
                                "mxfp4/b32 [16,8192,128], nvfp4/b16 [16,2048,512]" % E,
@@ -248,15 +295,112 @@ def main():
                    "launch": "eager" if graph is None else "hip_graph (one step captured, replayed K times)"},
         "eager_GBps": round(step_bytes * args.steps / eager_wall / 1e9, 1),
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
-        "fp4_sweep_GBps": round(fp4_bytes / (fp4_ms * 1e-3) / 1e9, 1),
+        "fp4_sweep_GBps": round(fp4_bytes / fp4_s / 1e9, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "reference_kernels": ref,
         "grouped_gemm": gemm,
         "extra_ops": extra,
         "ops": ops,
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(out), flush=True)
+
+
+CACHE_SETS = 8
+CACHE_CYCLES = 4     # passes over the rotating sets in one timed graph
+
+
+def time_graphs_interleaved(torch, fns_by_name, reps):
+    """Seconds for one pass over each list of launches: each list captured
+    once as a HIP graph; the graphs are replayed in turn, `reps` rounds, each
+    replay between two HIP events on the launch stream (so every operation is
+    timed among the others, as in the step, rather than after a long run of
+    itself); the mean over the rounds."""
+    graphs = {}
+    for name, fns in fns_by_name.items():
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        g.replay()
+        graphs[name] = g
+    torch.cuda.synchronize()
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)] for n in graphs}
+    for r in range(reps):
+        for n, g in graphs.items():
+            ev[n][r][0].record()
+            g.replay()
+            ev[n][r][1].record()
+    torch.cuda.synchronize()
+    out = {n: sum(a.elapsed_time(b) for a, b in ev[n]) * 1e-3 / reps for n in graphs}
+    del graphs
+    return out
+
+
+def time_graph(torch, fns, reps):
+    """Seconds for one pass over `fns` (kernel launches on the current
+    stream), captured once as a HIP graph and replayed `reps` times back to
+    back between two HIP events on that stream."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / reps
+    del g
+    return t
+
+
+def reference_rates(torch, dev, x, y, reps):
+    """The practical HBM ceiling: the plain copy, read-only and write-only
+    reference kernels (libmxq_roofline; same 16-byte non-temporal accesses and
+    wave tiles as the codec kernels, no arithmetic), each at the best of
+    unroll 1, 2 and 4, timed as graphs of back-to-back launches.  Sizes: one
+    sweep chunk (1.06 GB read + 1.06 GB written for the copy), and copies
+    that move 256 MiB and 64 MiB (the cache round trips' sizes) over eight
+    rotating sets, so that none is served from the last-level cache.  The
+    buffers are disjoint slices of the sweep's input and output tensors."""
+    from fp8_quantize_pack_amd import roofline as rl
+    xb, yb = x.view(-1).view(torch.uint8), y.view(-1).view(torch.uint8)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {"copy": {}, "read": {}, "write": {}}
+
+    def best(kind, name, moved, fns_for):
+        res = None
+        for u in (1, 2, 4):
+            fns = fns_for(u)
+            t = time_graph(torch, fns, reps) / len(fns)
+            r = {"bytes_per_launch": moved, "avg_launch_us": round(t * 1e6, 2),
+                 "GBps": round(moved / t / 1e9, 1), "unroll": u}
+            if res is None or r["GBps"] > res["GBps"]:
+                res = r
+        res["frac_of_peak"] = round(res["GBps"] / PEAK_HBM_GBPS, 4)
+        out[kind][name] = res
+
+    n = CALIBRATION_BYTES
+    best("copy", "sweep_chunk", 2 * n, lambda u: [lambda: rl.copy(xb[:n], yb[:n], u)])
+    for name, half in (("cache_256MiB", 128 << 20), ("cache_64MiB", 32 << 20)):
+        sets = [(xb[i * half:(i + 1) * half], yb[i * half:(i + 1) * half]) for i in range(CACHE_SETS)]
+        best("copy", name, 2 * half,
+             lambda u, sets=sets: [lambda s=s, d=d: rl.copy(s, d, u) for s, d in sets])
+    best("read", "sweep_chunk", n, lambda u: [lambda: rl.read(xb[:n], sink, u)])
+    best("write", "sweep_chunk", n, lambda u: [lambda: rl.fill(yb[:n], 0, u)])
+    return out
 
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
@@ -271,7 +415,14 @@ def grouped_gemm(torch, mxq, dev, reps):
     around `reps` launches each; not part of `value`.  For context each entry
     also times torch.bmm on the same per-expert products with dense bfloat16
     weights (the vendor BLAS, nothing to dequantize): a practical MFMA rate
-    for these shapes, not a result of this library."""
+    for these shapes, not a result of this library; and the pages' own
+    unfused design: this library's dequantization of every expert's weights
+    to bfloat16 [E, N, K], then that dense product.  In the backward product
+    (x @ W_e) the dequantized tensor is the right operand as it is.  The
+    forward product (x @ W_e^T) would read it through a transposed view,
+    which torch's bfloat16 bmm has faulted on with this software stack, so the
+    composition there multiplies by the same buffer viewed as [E, K, N]: the
+    same GEMM shape and bytes on a contiguous operand, timed for cost only."""
     g = torch.Generator(device=dev).manual_seed(11)
     out = {"peak_TFLOPs": PEAK_BF16_TFLOPS, "bound": "mfma", "dtype": "bf16"}
     for fmt, E, N, K, per in (("mxfp4", 32, 4096, 2048, 512), ("nvfp4", 64, 3072, 4096, 256)):
@@ -312,12 +463,27 @@ def grouped_gemm(torch, mxq, dev, reps):
             torch.cuda.synchronize()
             td = a.elapsed_time(b) / reps * 1e-3
             tfd = 2.0 * T * N * K / td / 1e12
-            del wd, yd
+            del wd
+            # the unfused design: dequantize all weights, then the dense product
+            wq = torch.empty(E, N, K, device=dev, dtype=torch.bfloat16)
+            if fmt == "mxfp4":
+                deq = lambda: mxq.mxq_dequantize_mxfp4(packed.view(torch.int8), scales, wq)
+            else:
+                deq = lambda: mxq.mxq_dequantize_nvfp4(packed, scales, rs, wq)
+            wr = wq if tr else wq.view(E, K, N)
+            comp = lambda: (deq(), torch.bmm(xd, wr, out=yd))
+            t_deq = _time_launches(torch, deq, reps)
+            t_comp = _time_launches(torch, comp, reps)
+            del wq, wr, yd
             out[f"{fmt}_{'backward' if tr else 'forward'}"] = {
                 "experts": E, "N": N, "K": K, "tokens": T, "avg_launch_us": round(t * 1e6, 1),
                 "TFLOPs": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                 "torch_bmm_dense_bf16_TFLOPs": round(tfd, 1),
-                "vs_torch_bmm_dense": round(tf / tfd, 3)}
+                "torch_bmm_dense_us": round(td * 1e6, 1),
+                "vs_torch_bmm_dense": round(tf / tfd, 3),
+                "dequant_us": round(t_deq * 1e6, 1),
+                "dequant_then_bmm_us": round(t_comp * 1e6, 1),
+                "speedup_vs_dequant_then_bmm": round(t_comp / t, 3)}
     return out
 
 
@@ -436,31 +602,57 @@ def extra_ops(torch, mxq, synth, dev, x, y, reps):
     return out
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x_gpu, budget_s: float):
-    """The CPU oracle, as it is, on whole rows of the same sweep until the time
-    budget is spent; all four weight operations per row batch, one thread."""
+    """The CPU oracle, as it is, on a bounded sample of the same sweep: every
+    16th batch of 256 rows, gathered until about `budget_s` seconds of
+    single-thread work (estimated from the first batch), all four weight
+    operations.  Timed twice on the same sample: on one thread, and on every
+    thread the oracle's OpenMP row loops get on this host (OMP_NUM_THREADS, or
+    all CPUs the process may run on).  `value` is the all-thread rate."""
     import torch
     import oracle
     K = x_gpu.shape[-1]
     rows = x_gpu.reshape(-1, K)
     batch = 256
-    done_rows, secs, nbytes = 0, 0.0, 0
-    start = 0
-    while secs < budget_s and start < rows.shape[0]:
-        xs = rows[start:start + batch].cpu()
+
+    def run(xs):
         t = time.perf_counter()
         p, s = oracle.quantize_mxfp4(xs)
         oracle.dequantize_mxfp4(p, s, torch.bfloat16)
         p, s, g = oracle.quantize_nvfp4(xs)
         oracle.dequantize_nvfp4(p, s, g, torch.bfloat16)
-        secs += time.perf_counter() - t
-        n = xs.numel()
-        nbytes += 2 * bytes_mx(n) + 2 * bytes_nv(n, xs.shape[0])
-        done_rows += xs.shape[0]
-        start += batch * 16   # spread the sample over the tensor
-    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done_rows} rows x 7168 of the sweep (every 16th 256-row batch), "
-                      f"MXFP4+NVFP4 quantize and dequantize, {secs:.1f} s single-threaded"}
+        return time.perf_counter() - t
+
+    all_threads = oracle.max_threads()
+    oracle.set_threads(1)
+    first = rows[:batch].cpu()
+    t1 = run(first)
+    nb = max(1, min(int(budget_s / max(t1, 1e-6)), rows.shape[0] // (batch * 16)))
+    idx = torch.cat([torch.arange(b * batch * 16, b * batch * 16 + batch) for b in range(nb)])
+    xs = rows[idx.to(rows.device)].cpu()
+    n = xs.numel()
+    nbytes = 2 * bytes_mx(n) + 2 * bytes_nv(n, xs.shape[0])
+    secs1 = run(xs)
+    oracle.set_threads(all_threads)
+    secsn = run(xs)
+    return {"value": round(nbytes / secsn / 1e9, 4), "unit": "GB/s", "cores": all_threads,
+            "kind": "oracle",
+            "sample": f"{xs.shape[0]} rows x {K} of the sweep (every 16th 256-row batch), MXFP4 and "
+                      f"NVFP4 quantize and dequantize, {nbytes} algorithmic bytes: "
+                      f"{secsn:.2f} s on {all_threads} threads, {secs1:.1f} s on 1 thread",
+            "single_thread_value": round(nbytes / secs1 / 1e9, 4),
+            "threads": all_threads, "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": _cpu_model()}
 
 
 if __name__ == "__main__":

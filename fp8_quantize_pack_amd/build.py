@@ -1,7 +1,8 @@
 """Build libmxq.so (HIP, gfx950) in-tree with hipcc.
 
 Every HIP source is compiled to an object in parallel, then linked into
-``fp8_quantize_pack_amd/libmxq.so``.  Flags that matter for bit-exactness:
+``fp8_quantize_pack_amd/libmxq.so``; the streaming reference kernels that
+measure the practical HBM ceiling go into ``libmxq_roofline.so``.  Flags that matter for bit-exactness:
 no fast-math, no contraction of a*b+c into fma (the kernels call fmaf
 explicitly where they want one), correctly rounded float32 division, and
 denormals kept.  Packed-FP32 instructions are disabled.
@@ -17,12 +18,14 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmxq.so")
+ROOFLINE_LIB = os.path.join(HERE, "libmxq_roofline.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["mxq_api.cpp", "k_mxfp4.hip", "k_nvfp4.hip", "k_cache.hip",
            "mxq_api_gemm.cpp", "k_grouped_mm.hip",
            "mxq_api_ext.cpp", "k_mxfp8.hip", "k_fp4_static.hip", "k_kv.hip"]
+ROOFLINE_SOURCES = ["k_roofline_ref.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC",
@@ -44,7 +47,7 @@ def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
     out_dir = os.path.join(HERE, "_build")
     os.makedirs(out_dir, exist_ok=True)
     procs = []
-    for src in SOURCES:
+    for src in SOURCES + ROOFLINE_SOURCES:
         path = os.path.join(CSRC, src)
         lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
         cmd = [HIPCC, *lang, f"--offload-arch={ARCH}", *COMMON, *extra_flags,
@@ -63,11 +66,12 @@ def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
     if failed:
         msg = "\n".join(f"--- {s}\n{l}" for s, l in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = out + ".tmp"
-    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-            *[_obj(s, out_dir) for s in SOURCES]]
-    subprocess.run(link, check=True)
-    os.replace(tmp, out)
+    for target, srcs in ((out, SOURCES), (ROOFLINE_LIB, ROOFLINE_SOURCES)):
+        tmp = target + ".tmp"
+        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+                *[_obj(s, out_dir) for s in srcs]]
+        subprocess.run(link, check=True)
+        os.replace(tmp, target)
     return out
 
 

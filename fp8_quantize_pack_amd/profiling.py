@@ -14,8 +14,9 @@ with ``--calibrate-copy``)::
         DIR_W/write_counter_collection.csv OUT.txt --copy-bytes N --command-fetch "..." --command-write "..."
 
 FETCH_SIZE and WRITE_SIZE are KiB per dispatch.  Each is scaled by the
-factor that maps the same counter, read on the calibration kernel (a torch
-elementwise negation that reads N bytes and writes N bytes), to N: the
+factor that maps the same counter, read on the calibration kernel (the
+reference copy kernel of libmxq_roofline, which reads N bytes and writes N
+bytes), to N: the
 traffic of a kernel is fetch * 1024 * f_fetch + write * 1024 * f_write bytes
 per launch, averaged over its dispatches.  The traffic file names the hash of
 the kernel sources it was taken on; bench.py uses it only while the sources
@@ -53,8 +54,17 @@ BENCH_KERNELS = {
     "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1, 128>",
     "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0, 128>",
     "gemm_nvfp4_backward": "mxq::gmm::k_grouped_mm<2, 1, 128>",
+    "ref_copy_u1": "(anonymous namespace)::k_copy<1>",
+    "ref_copy_u2": "(anonymous namespace)::k_copy<2>",
+    "ref_copy_u4": "(anonymous namespace)::k_copy<4>",
+    "ref_read_u1": "(anonymous namespace)::k_read<1>",
+    "ref_read_u2": "(anonymous namespace)::k_read<2>",
+    "ref_read_u4": "(anonymous namespace)::k_read<4>",
+    "ref_write_u1": "(anonymous namespace)::k_fill<1>",
+    "ref_write_u2": "(anonymous namespace)::k_fill<2>",
+    "ref_write_u4": "(anonymous namespace)::k_fill<4>",
 }
-CALIBRATION_MARK = "neg_kernel"
+CALIBRATION_MARK = "k_copy<2>"
 
 
 # the sources that decide what the codec kernels bench.py measures execute
@@ -157,7 +167,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_bytes: int,
         f"# command (fetch): {cmd_fetch}",
         f"# command (write): {cmd_write}",
         f"source_hash: {kernel_source_hash()}",
-        f"# calibration: torch neg over {copy_bytes} bytes read + {copy_bytes} bytes written reads "
+        f"# calibration: the reference copy over {copy_bytes} bytes read + {copy_bytes} bytes written reads "
         f"FETCH_SIZE {cal_f[0][0]:.0f} KiB (factor {f_fetch:.4f}), WRITE_SIZE {cal_w[0][0]:.0f} KiB (factor {f_write:.4f})",
         "# per op: scaled fetch + write bytes per launch (mean over dispatches) vs the algorithmic bytes per launch",
     ]
