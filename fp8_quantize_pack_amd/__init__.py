@@ -45,7 +45,7 @@ NVFP4_BLOCK_SIZE = 16
 _STATUS = {
     0: "MXQ_OK", 1: "MXQ_E_NULL", 2: "MXQ_E_SHAPE", 3: "MXQ_E_DTYPE",
     4: "MXQ_E_FORMAT", 5: "MXQ_E_BLOCK", 6: "MXQ_E_SIZE", 7: "MXQ_E_LAUNCH",
-    8: "MXQ_E_MODE", 9: "MXQ_E_ALIGN",
+    8: "MXQ_E_MODE", 9: "MXQ_E_ALIGN", 10: "MXQ_E_SCRATCH",
 }
 
 
@@ -68,11 +68,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.mxq_fake_quantize_fp4_static.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp]
     L.mxq_dequantize_kv_pages_nvfp4.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, i32, vp]
     L.mxq_quantize_kv_nvfp4.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp, vp, vp]
+    L.mxq_quantize_kv_nvfp4_noalloc.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp, vp]
     for f in ("mxq_quantize_mxfp4", "mxq_dequantize_mxfp4", "mxq_quantize_nvfp4",
               "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_grouped_mm_mxfp4",
               "mxq_grouped_mm_nvfp4", "mxq_quantize_mxfp8", "mxq_dequantize_mxfp8",
               "mxq_fake_quantize_fp4_static", "mxq_dequantize_kv_pages_nvfp4",
-              "mxq_quantize_kv_nvfp4"):
+              "mxq_quantize_kv_nvfp4", "mxq_quantize_kv_nvfp4_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     L.mxq_status_string.argtypes = [ctypes.c_int]
     L.mxq_status_string.restype = ctypes.c_char_p
@@ -332,6 +333,26 @@ def mxq_quantize_kv_nvfp4(k, head_amax, packed, scales, row_scale, smooth=True,
                                      _ptr(head_amax), _ptr(packed), _ptr(scales),
                                      _ptr(row_scale), _stream(k, stream)),
            "mxq_quantize_kv_nvfp4")
+
+
+def mxq_quantize_kv_nvfp4_noalloc(k, packed, scales, row_scale, smooth=True,
+                                  stream=None) -> None:
+    """mxq_quantize_kv_nvfp4 with the per-head scratch in the library's static
+    device array (no workspace argument; at most NOALLOC_KV_MAX_HEADS heads)."""
+    S, H, D = k.shape[-3], k.shape[-2], k.shape[-1]
+    S = k.numel() // (H * D) if k.numel() else 0
+    c = "mxq_quantize_kv_nvfp4_noalloc"
+    _buf(k, k.numel() * k.element_size(), "k", c)
+    _buf(packed, S * H * D // 2, "packed", c)
+    _buf(scales, S * H * D // 16, "scales", c)
+    _buf(row_scale, 4 * S * H, "row_scale", c)
+    _check(lib.mxq_quantize_kv_nvfp4_noalloc(_ptr(k), _dt(k.dtype), S, H, D, int(bool(smooth)),
+                                             _ptr(packed), _ptr(scales), _ptr(row_scale),
+                                             _stream(k, stream)),
+           c)
+
+
+NOALLOC_KV_MAX_HEADS = 1024    # MXQ_NOALLOC_KV_MAX_HEADS
 
 
 # ------------------------------------------------------------------ tensor API

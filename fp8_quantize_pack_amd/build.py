@@ -24,7 +24,8 @@ ARCH = "gfx950"
 
 SOURCES = ["mxq_api.cpp", "k_mxfp4.hip", "k_nvfp4.hip", "k_cache.hip",
            "mxq_api_gemm.cpp", "k_grouped_mm.hip",
-           "mxq_api_ext.cpp", "k_mxfp8.hip", "k_fp4_static.hip", "k_kv.hip"]
+           "mxq_api_ext.cpp", "k_mxfp8.hip", "k_fp4_static.hip", "k_kv.hip",
+           "mxq_api_noalloc.hip"]
 ROOFLINE_SOURCES = ["k_roofline_ref.hip"]
 
 COMMON = [

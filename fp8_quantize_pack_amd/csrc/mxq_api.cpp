@@ -26,6 +26,7 @@ const char* mxq_status_string(mxq_status s) {
     case MXQ_E_LAUNCH: return "kernel launch failed";
     case MXQ_E_MODE: return "unknown NVFP4 scale mode";
     case MXQ_E_ALIGN: return "pointer not 16-byte aligned";
+    case MXQ_E_SCRATCH: return "the call needs more than its static device scratch";
   }
   return "unknown status";
 }

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 1
+#define MXQ_ABI_VERSION 2
 
 /* Floating element types of inputs and dequantized outputs ([mxfp4 page]
  * and [nvfp4 page] take any floating-point tensor). */
@@ -104,7 +104,8 @@ typedef enum mxq_status {
   MXQ_E_SIZE = 6,    /* rows * K overflows int64                             */
   MXQ_E_LAUNCH = 7,  /* the HIP runtime rejected a kernel launch             */
   MXQ_E_MODE = 8,    /* unknown mxq_nv_mode                                  */
-  MXQ_E_ALIGN = 9    /* a pointer is not 16-byte aligned where required      */
+  MXQ_E_ALIGN = 9,   /* a pointer is not 16-byte aligned where required      */
+  MXQ_E_SCRATCH = 10 /* the call needs more than its static device scratch   */
 } mxq_status;
 
 /*
@@ -290,6 +291,27 @@ mxq_status mxq_quantize_kv_nvfp4(const void* k, mxq_dtype dt, int64_t tokens, in
                                  int64_t head_dim, int32_t smooth, float* head_amax,
                                  uint8_t* packed, uint8_t* scales, float* row_scale,
                                  hipStream_t stream);
+
+/*
+ * mxq_quantize_kv_nvfp4 without the head_amax workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, validation,
+ * kernels and results as mxq_quantize_kv_nvfp4, minus head_amax: the per-head
+ * maxima are gathered in a static device array that the library holds on
+ * each GPU it runs on until the process ends (heads * 32 float32 words,
+ * 128 KiB at the limit).
+ *   heads > MXQ_NOALLOC_KV_MAX_HEADS returns MXQ_E_SCRATCH (before any launch).
+ *   The call allocates nothing; the first call on a device looks up the
+ *   array's device address (hipGetSymbolAddress) and keeps it.
+ *   Every call on one GPU uses the same array: calls that overlap in time on
+ *   one GPU (different streams) race and give unspecified results; calls in
+ *   stream order are independent (each clears the words it uses).
+ */
+#define MXQ_NOALLOC_KV_MAX_HEADS 1024
+mxq_status mxq_quantize_kv_nvfp4_noalloc(const void* k, mxq_dtype dt, int64_t tokens,
+                                         int64_t heads, int64_t head_dim, int32_t smooth,
+                                         uint8_t* packed, uint8_t* scales, float* row_scale,
+                                         hipStream_t stream);
 
 /*
  * Grouped GEMM over packed fp4 expert weights, dequantized on the fly

@@ -10,8 +10,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "mxq.h")).read()
+def _declared_functions(header="mxq.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", src)))
 
@@ -22,7 +22,8 @@ def test_header_declares_the_operations():
               "mxq_dequantize_nvfp4", "mxq_quantize_cache", "mxq_grouped_mm_mxfp4",
               "mxq_grouped_mm_nvfp4", "mxq_quantize_mxfp8", "mxq_dequantize_mxfp8",
               "mxq_fake_quantize_fp4_static", "mxq_dequantize_kv_pages_nvfp4",
-              "mxq_quantize_kv_nvfp4", "mxq_status_string", "mxq_abi_version"):
+              "mxq_quantize_kv_nvfp4", "mxq_quantize_kv_nvfp4_noalloc", "mxq_status_string",
+              "mxq_abi_version"):
         assert n in names
 
 
@@ -30,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     import fp8_quantize_pack_amd as mxq
     for n in _declared_functions():
         assert hasattr(mxq.lib, n), n
-    assert mxq.abi_version() == 1
+    assert mxq.abi_version() == 2
 
 
 @pytest.fixture(scope="module")
@@ -160,7 +161,7 @@ def test_kv_validation(L):
 
 
 def test_status_strings(L):
-    for s in range(10):
+    for s in range(11):
         assert L.mxq_status_string(s)
     assert L.mxq_status_string(99) == b"unknown status"
 
@@ -281,3 +282,44 @@ def test_c_abi_wrappers_check_every_buffer_size():
         mxq.mxq_grouped_mm_nvfp4(torch.zeros(64, 256, dtype=torch.bfloat16), pk, u8(4, 128, 16),
                                  torch.ones(4, 128), torch.zeros(4, dtype=torch.int32),
                                  torch.zeros(64, 256, dtype=torch.bfloat16))
+
+
+def test_every_header_is_covered():
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == \
+        ["mxq.h", "mxq_roofline.h"]
+
+
+def test_roofline_library_exports_and_validation():
+    """The streaming reference kernels (measurement only): every declared
+    symbol is exported, and bad arguments return their status before any
+    launch."""
+    from fp8_quantize_pack_amd import roofline
+    L = roofline.lib()
+    names = _declared_functions("mxq_roofline.h")
+    assert names == ["mxq_ref_copy", "mxq_ref_fill", "mxq_ref_read"]
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.mxq_ref_copy(FAKE, FAKE, 24, 2, None) == 2          # not a multiple of 16
+    assert L.mxq_ref_copy(FAKE, FAKE, -16, 2, None) == 2
+    assert L.mxq_ref_copy(FAKE, FAKE, 64, 3, None) == 5          # unroll
+    assert L.mxq_ref_copy(None, FAKE, 64, 2, None) == 1
+    assert L.mxq_ref_copy(FAKE, FAKE + 8, 64, 2, None) == 9
+    assert L.mxq_ref_copy(None, None, 0, 2, None) == 0           # empty: no launch
+    assert L.mxq_ref_read(FAKE, 64, 2, 0, None, None) == 1       # no sink
+    assert L.mxq_ref_read(FAKE + 4, 64, 2, 0, FAKE, None) == 9
+    assert L.mxq_ref_fill(FAKE, 40, 0, 2, None) == 2
+    assert L.mxq_ref_fill(FAKE, 64, 0, 16, None) == 5
+
+
+def test_noalloc_validation(L):
+    f = L.mxq_quantize_kv_nvfp4_noalloc
+    # k, dt, S, H, D, smooth, packed, scales, row_scale, stream
+    assert f(FAKE, 1, 64, 1025, 128, 1, FAKE, FAKE, FAKE, None) == 10   # beyond the static scratch
+    assert f(FAKE, 1, 64, 5000, 128, 1, FAKE, FAKE, FAKE, None) == 2
+    assert f(FAKE, 1, 64, 8, 96, 1, FAKE, FAKE, FAKE, None) == 2
+    assert f(FAKE, 9, 64, 8, 128, 1, FAKE, FAKE, FAKE, None) == 3
+    assert f(FAKE, 1, 64, 8, 128, 2, FAKE, FAKE, FAKE, None) == 8
+    assert f(None, 1, 64, 8, 128, 1, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE + 4, 1, 64, 8, 128, 1, FAKE, FAKE, FAKE, None) == 9
+    assert f(None, 1, 0, 8, 128, 1, None, None, None, None) == 0
+    assert L.mxq_status_string(10) == b"the call needs more than its static device scratch"
