@@ -112,10 +112,12 @@ def kernel_source_hash() -> str:
 
 
 def short_name(name: str) -> str:
+    """Kernel name without its return type and parameter list."""
     name = name.strip()
     if name.startswith("void "):
         name = name[5:]
-    return name.split("(")[0]
+    anon = "(anonymous namespace)"
+    return name.replace(anon, "\0").split("(")[0].replace("\0", anon)
 
 
 def summarize_trace(stats_csv: str, command: str) -> str:
