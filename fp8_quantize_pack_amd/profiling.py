@@ -142,22 +142,60 @@ def summarize_trace(stats_csv: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def _counter_means(path: str, counter: str):
-    """Mean counter value per dispatch, by kernel."""
+def summarize_trace_dispatches(trace_csv: str, command: str) -> str:
+    """Per bench op, its dispatches grouped by grid size (one line per
+    size: the sweep's 36- and 4-expert chunks, the cache tensors, and any
+    other size the bench launches the same kernel at), from rocprofv3's
+    per-dispatch kernel trace."""
+    groups = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        k = short_name(r["Kernel_Name"])
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        groups[(k, grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = [
+        "# rocprofv3 kernel trace of bench.py (one MI355X): launch durations per kernel and grid size",
+        f"# command: {command}",
+        f"# kernel_source_hash: {kernel_source_hash()}",
+        "# durations in microseconds; grid = work-items of the dispatch",
+        f"{'op':24s} {'grid':>10s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}",
+    ]
+    for op, k in BENCH_KERNELS.items():
+        for (kk, grid), ts in sorted(groups.items(), key=lambda g: -g[0][1]):
+            if kk != k:
+                continue
+            out.append(f"{op:24s} {grid:10d} {len(ts):6d} {sum(ts) / len(ts):9.2f} "
+                       f"{min(ts):9.2f} {max(ts):9.2f}")
+    return "\n".join(out) + "\n"
+
+
+def _grid(r) -> int:
+    if "Grid_Size" in r:
+        return int(float(r["Grid_Size"]))
+    return 0
+
+
+def _counter_means(path: str, counter: str, only_grids=None):
+    """Mean counter value per dispatch, by kernel.  only_grids maps a kernel
+    to the grid sizes (work-items) whose dispatches count for it (the bench
+    launches some kernels at other sizes too)."""
     acc = defaultdict(lambda: [0.0, 0])
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
         k = short_name(r["Kernel_Name"])
+        if only_grids and k in only_grids and _grid(r) not in only_grids[k]:
+            continue
         acc[k][0] += float(r["Counter_Value"])
         acc[k][1] += 1
     return {k: (s / n, n) for k, (s, n) in acc.items()}
 
 
 def summarize_traffic(fetch_csv: str, write_csv: str, copy_bytes: int,
-                      cmd_fetch: str, cmd_write: str, algorithmic: dict) -> str:
-    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
-    write = _counter_means(write_csv, "WRITE_SIZE")
+                      cmd_fetch: str, cmd_write: str, algorithmic: dict,
+                      only_grids=None) -> str:
+    og = {BENCH_KERNELS[op]: g for op, g in (only_grids or {}).items()}
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE", og)
+    write = _counter_means(write_csv, "WRITE_SIZE", og)
     cal_f = [v for k, v in fetch.items() if CALIBRATION_MARK in k]
     cal_w = [v for k, v in write.items() if CALIBRATION_MARK in k]
     if not cal_f or not cal_w:
@@ -173,6 +211,8 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_bytes: int,
         f"FETCH_SIZE {cal_f[0][0]:.0f} KiB (factor {f_fetch:.4f}), WRITE_SIZE {cal_w[0][0]:.0f} KiB (factor {f_write:.4f})",
         "# per op: scaled fetch + write bytes per launch (mean over dispatches) vs the algorithmic bytes per launch",
     ]
+    for op, g in sorted((only_grids or {}).items()):
+        out.append(f"# {op}: only dispatches of grid sizes {sorted(g)} (the sweep's chunks)")
     for op, k in BENCH_KERNELS.items():
         if k not in fetch or k not in write:
             continue
@@ -185,25 +225,92 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_bytes: int,
     return "\n".join(out) + "\n"
 
 
+CU_NUM = 256      # compute units of one MI355X
+XCD_NUM = 8       # GRBM_GUI_ACTIVE is reported summed over the XCDs
+
+
+def summarize_counters(csvs, command: str, elements: dict) -> str:
+    """Per bench op: mean per dispatch of every counter in the given
+    rocprofv3 --pmc CSV files (one pass each), and the derived
+    VALUBusy = 100 * SQ_ACTIVE_INST_VALU / CU_NUM / (GRBM_GUI_ACTIVE / XCD_NUM)
+    (rocprof's own formula, with the GPU-busy cycles of one XCD), the VALU
+    issue per CU cycle, wave-instructions x 64 lanes per element, and the
+    share of wave time spent waiting for any instruction to issue."""
+    means = defaultdict(dict)
+    for path in csvs:
+        acc = defaultdict(lambda: [0.0, 0])
+        for r in csv.DictReader(open(path)):
+            k = (short_name(r["Kernel_Name"]), r["Counter_Name"])
+            acc[k][0] += float(r["Counter_Value"])
+            acc[k][1] += 1
+        for (k, c), (tot, n) in acc.items():
+            means[k][c] = tot / n
+    out = [
+        "# rocprofv3 counters per dispatch (one MI355X), mean over the op's dispatches",
+        f"# command: {command}",
+        f"source_hash: {kernel_source_hash()}",
+        "# VALUBusy% = 100 * SQ_ACTIVE_INST_VALU / 256 / (GRBM_GUI_ACTIVE / 8); "
+        "valu_per_cu_cycle = SQ_INSTS_VALU / 256 / (GRBM_GUI_ACTIVE / 8); "
+        "valu_lane_ops_per_elem = 64 * SQ_INSTS_VALU / elements; wait% = 100 * SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+    ]
+    for op, k in BENCH_KERNELS.items():
+        m = means.get(k)
+        if not m:
+            continue
+        parts = []
+        grbm = m.get("GRBM_GUI_ACTIVE")
+        if grbm and "SQ_ACTIVE_INST_VALU" in m:
+            parts.append(f"VALUBusy%: {100 * m['SQ_ACTIVE_INST_VALU'] / CU_NUM / (grbm / XCD_NUM):.1f}")
+        if grbm and "SQ_INSTS_VALU" in m:
+            parts.append(f"valu_per_cu_cycle: {m['SQ_INSTS_VALU'] / CU_NUM / (grbm / XCD_NUM):.3f}")
+        if op in elements and "SQ_INSTS_VALU" in m:
+            parts.append(f"valu_lane_ops_per_elem: {64 * m['SQ_INSTS_VALU'] / elements[op]:.2f}")
+        if "SQ_WAIT_INST_ANY" in m and m.get("SQ_WAVE_CYCLES"):
+            parts.append(f"wait%: {100 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1f}")
+        out.append(f"{op} " + "  ".join(parts))
+        out.append("    " + "  ".join(f"{c}: {v:.0f}" for c, v in sorted(m.items())))
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
     t = sub.add_parser("trace")
     t.add_argument("stats_csv"); t.add_argument("out"); t.add_argument("--command", required=True)
+    t.add_argument("--dispatches", default=None,
+                   help="the per-dispatch kernel_trace.csv: add durations per grid size")
     c = sub.add_parser("traffic")
     c.add_argument("fetch_csv"); c.add_argument("write_csv"); c.add_argument("out")
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--command-fetch", required=True); c.add_argument("--command-write", required=True)
     c.add_argument("--algorithmic", default="", help="op=bytes,... algorithmic bytes per launch")
+    c.add_argument("--only-grids", default="", help="op=g1:g2,... grid sizes that count for op")
+    q = sub.add_parser("counters")
+    q.add_argument("out"); q.add_argument("csvs", nargs="+")
+    q.add_argument("--command", required=True)
+    q.add_argument("--elements", default="", help="op=elements,... elements per launch")
     a = ap.parse_args()
     if a.what == "trace":
         txt = summarize_trace(a.stats_csv, a.command)
+        if a.dispatches:
+            txt += "\n" + summarize_trace_dispatches(a.dispatches, a.command)
+    elif a.what == "counters":
+        el = {}
+        for kv in filter(None, a.elements.split(",")):
+            k, v = kv.split("=")
+            el[k] = float(v)
+        txt = summarize_counters(a.csvs, a.command, el)
     else:
         alg = {}
         for kv in filter(None, a.algorithmic.split(",")):
             k, v = kv.split("=")
             alg[k] = float(v)
-        txt = summarize_traffic(a.fetch_csv, a.write_csv, a.copy_bytes, a.command_fetch, a.command_write, alg)
+        og = {}
+        for kv in filter(None, a.only_grids.split(",")):
+            k, v = kv.split("=")
+            og[k] = {int(x) for x in v.split(":")}
+        txt = summarize_traffic(a.fetch_csv, a.write_csv, a.copy_bytes, a.command_fetch,
+                                a.command_write, alg, og)
     with open(a.out, "w") as f:
         f.write(txt)
     print(txt, end="")
