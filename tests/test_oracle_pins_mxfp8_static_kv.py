@@ -7,6 +7,19 @@ arithmetic (library routines), from special cases that reduce to oracle
 functions already pinned there (NVFP4 with a given scale, the mxfp4 cache
 round trip), from hand-derived closed forms, and from characterising
 properties.
+
+Parity unpinned by the pages, for two readings these tests pin the oracle to
+without the pages fixing them:
+  * static two-level FP4: the pages name the e4m3 fake quantization of the
+    block scale (scaled_e4m3 under the per-tensor amax) without printing its
+    arithmetic.  The oracle takes it as multiply by 448 / P, cast, divide by
+    448 / P.  Most pins use a global amax for which 448 / P is a power of two,
+    where every ordering of those steps gives the same bits; only the 1e-8
+    floor case and the error bound reach a general P.
+  * k_smooth: the pages compute the row mean with torch's mean, whose
+    summation order torch does not fix.  The oracle sums pairwise (halves,
+    recursively); the pins check that order on hand cases where it matters
+    and the bf16 rounding bound that any order meets.
 """
 import math
 
