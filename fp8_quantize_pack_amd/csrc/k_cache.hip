@@ -90,12 +90,21 @@ __device__ __forceinline__ void cache_chunk(const Raw8<DT>& raw, bool ok, void* 
   if (ok) st8<DT>(y, c, o);
 }
 
-// Row groups in flight per wave (their loads are issued together).
+// Row groups in flight per wave (their loads are issued together).  One,
+// with two row groups per wave in turn, measured fastest on the 32 to 128 MiB
+// KV tensors (graphs of back-to-back launches over cold inputs): fp8 block
+// 32 [16, 8192, 512] 43.4 us against 46.4 with two in flight, mxfp4 block 32
+// [16, 8192, 128] 12.9 against 13.5 (the plain copy of the same bytes takes
+// 12.2 to 12.9), nvfp4 block 16 [16, 2048, 512] unchanged at 13.7; four in
+// flight was slower for all three.
 #ifndef MXQ_CACHE_UNROLL
-#define MXQ_CACHE_UNROLL 2
+#define MXQ_CACHE_UNROLL 1
 #endif
 constexpr int kCacheUnroll = MXQ_CACHE_UNROLL;
-constexpr int64_t kCacheGroupsPerWave = 2 * kCacheUnroll;
+#ifndef MXQ_CACHE_GROUPS_PER_WAVE
+#define MXQ_CACHE_GROUPS_PER_WAVE (2 * MXQ_CACHE_UNROLL)
+#endif
+constexpr int64_t kCacheGroupsPerWave = MXQ_CACHE_GROUPS_PER_WAVE;
 
 template <int DT, int FMT, int B>
 __global__ __launch_bounds__(256) void k_cache_qdq(const void* __restrict__ x,

@@ -338,7 +338,10 @@ hipError_t launch_grouped_mm(const void* x, int64_t T, const uint8_t* packed,
   // the last tile exit at once), times the output tiles
   // 128-row token tiles (256-row tiles need 280 registers per lane, one wave
   // per SIMD, and measured slower)
-  constexpr int bm = 128;
+#ifndef MXQ_GMM_BM
+#define MXQ_GMM_BM 128
+#endif
+  constexpr int bm = MXQ_GMM_BM;
   const int64_t slots = (T + bm - 1) / bm + E;
   const int64_t ntc = C / gmm::BN;
   const dim3 grid((unsigned)(slots * ntc)), block(gmm::THREADS);
