@@ -221,13 +221,45 @@ __device__ __forceinline__ bool find_tile(const Args& a, int64_t slot, int64_t& 
   return e_out >= 0;
 }
 
+// Token tiles of all experts together (uniform over the workgroup): the sum
+// of ceil(group / BM) over the groups offs describes, clamped as find_tile
+// clamps them.
+template <int BM>
+__device__ __forceinline__ int64_t total_tiles(const Args& a) {
+  __shared__ int64_t s_part[THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int64_t sum = 0;
+  for (int64_t e = tid; e < a.E; e += THREADS) {
+    int64_t lo = e > 0 ? (int64_t)a.offs[e - 1] : 0;
+    int64_t hi = (int64_t)a.offs[e];
+    lo = lo < 0 ? 0 : (lo > a.T ? a.T : lo);
+    hi = hi < lo ? lo : (hi > a.T ? a.T : hi);
+    sum += (hi - lo + BM - 1) / BM;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+  if (lane == 0) s_part[wave] = sum;
+  __syncthreads();
+  int64_t tot = 0;
+#pragma unroll
+  for (int w = 0; w < THREADS / 64; ++w) tot += s_part[w];
+  return tot;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
-// L2.  Logical tile L = xcd-major renumbering of the workgroup id, so that one
-// XCD runs a contiguous range of logical tiles (a bijection for any count).
+// L2.  The grid is sized for the most token tiles the groups could need (the
+// host never reads offs), ceil(T / BM) + E per output tile; the G tiles that
+// exist are split evenly over the XCDs, each XCD taking a contiguous range of
+// logical tiles, and the surplus workgroups of every XCD exit.  (Numbering
+// all grid slots instead put every surplus slot on the last XCDs: a third of
+// the chip idle for 256 tokens per expert.)  Returns -1 for a surplus
+// workgroup.
 __device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t G) {
   constexpr int64_t X = 8;
   const int64_t xcd = b % X, pos = b / X, q = G / X, r = G % X;
-  return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
+  const int64_t cnt = q + (xcd < r ? 1 : 0);
+  if (pos >= cnt) return -1;
+  return xcd * q + (xcd < r ? xcd : r) + pos;
 }
 
 // Waves per SIMD the register allocation must allow.  Left to itself the
@@ -251,7 +283,8 @@ __global__ __launch_bounds__(THREADS) MXQ_GMM_OCCUPANCY void k_grouped_mm(Args a
   // logical tile -> (token slot, output tile), output tiles fastest: the
   // tiles that share an activation tile, and then those that share an
   // expert's weights, run next to each other on one XCD
-  const int64_t L = xcd_logical(blockIdx.x, gridDim.x);
+  const int64_t L = xcd_logical(blockIdx.x, total_tiles<BM>(a) * ntiles_c);
+  if (L < 0) return;                        // uniform over the workgroup
   const int64_t slot = L / ntiles_c;
   if (!find_tile<BM>(a, slot, e, m0, m1)) return;   // uniform over the workgroup
   const int64_t c0 = (L - slot * ntiles_c) * BN;
