@@ -262,17 +262,26 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t G) {
   return xcd * q + (xcd < r ? xcd : r) + pos;
 }
 
-// Waves per SIMD the register allocation must allow.  Left to itself the
-// compiler takes 156 registers (3 waves); at 4 it fits 128 with a few spills
-// outside the reduction loop, and the extra workgroup per CU keeps more
-// global loads in flight (NVFP4 6-10% faster, MXFP4 forward 2-4%).
+// Waves per SIMD the register allocation must allow.  128-row tiles: left to
+// itself the compiler takes 156 registers (3 waves); at 4 it fits 128 with a
+// few spills outside the reduction loop, and the extra workgroup per CU keeps
+// more global loads in flight (NVFP4 6-10% faster, MXFP4 forward 2-4%).
+// 256-row tiles: 236-248 registers without spills at 2 waves (at 3 or 4 the
+// accumulators move to AGPRs and the kernel runs one wave per SIMD).
 #ifndef MXQ_GMM_WAVES_PER_EU
 #define MXQ_GMM_WAVES_PER_EU 4
 #endif
-#define MXQ_GMM_OCCUPANCY __attribute__((amdgpu_waves_per_eu(MXQ_GMM_WAVES_PER_EU, MXQ_GMM_WAVES_PER_EU)))
+#ifndef MXQ_GMM_WAVES_PER_EU_256
+#define MXQ_GMM_WAVES_PER_EU_256 2
+#endif
+
+template <int BM>
+constexpr int gmm_waves_per_eu() { return BM == 256 ? MXQ_GMM_WAVES_PER_EU_256 : MXQ_GMM_WAVES_PER_EU; }
 
 template <int FMT, int TRANS, int BM>
-__global__ __launch_bounds__(THREADS) MXQ_GMM_OCCUPANCY void k_grouped_mm(Args a, int64_t ntiles_c) {
+__global__ __launch_bounds__(THREADS)
+__attribute__((amdgpu_waves_per_eu(gmm_waves_per_eu<BM>(), gmm_waves_per_eu<BM>())))
+void k_grouped_mm(Args a, int64_t ntiles_c) {
   constexpr int MT = BM / 64;               // 32 x 32 MFMA tiles per wave along the tokens
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
@@ -367,18 +376,27 @@ hipError_t launch_grouped_mm(const void* x, int64_t T, const uint8_t* packed,
   a.y = static_cast<uint16_t*>(y);
   a.T = T; a.E = E; a.N = N; a.K = K;
   const int64_t C = trans ? K : N;
-  // token-tile slots: at most ceil(T / bm) + E over all experts (slots past
-  // the last tile exit at once), times the output tiles
-  // 128-row token tiles (256-row tiles need 280 registers per lane, one wave
-  // per SIMD, and measured slower)
+  // Token-tile height: 256 rows when the experts average 256 tokens or more
+  // (each weight tile is dequantized once per 256 rows and every activation
+  // tile is read by half as many workgroups: on the MoE expert shapes with
+  // 256 and 512 tokens per expert 6-8% faster than 128-row tiles, except the
+  // NVFP4 backward, within 2%), else 128 rows (a 256-row tile of a small group
+  // would spend its MFMAs on rows that are not there).  The grid holds the
+  // most token tiles the groups could need, ceil(T / bm) + E per output tile
+  // (slots past the last tile exit at once).
 #ifndef MXQ_GMM_BM
-#define MXQ_GMM_BM 128
+#define MXQ_GMM_BM 0
 #endif
-  constexpr int bm = MXQ_GMM_BM;
+  const bool tall = MXQ_GMM_BM == 256 || (MXQ_GMM_BM == 0 && T >= 256 * E);
+  const int64_t bm = tall ? 256 : 128;
   const int64_t slots = (T + bm - 1) / bm + E;
   const int64_t ntc = C / gmm::BN;
   const dim3 grid((unsigned)(slots * ntc)), block(gmm::THREADS);
-#define MXQ_GMM_LAUNCH(F, TR) hipLaunchKernelGGL((gmm::k_grouped_mm<F, TR, bm>), grid, block, 0, s, a, ntc)
+#define MXQ_GMM_LAUNCH(F, TR)                                                               \
+  do {                                                                                     \
+    if (tall) hipLaunchKernelGGL((gmm::k_grouped_mm<F, TR, 256>), grid, block, 0, s, a, ntc); \
+    else hipLaunchKernelGGL((gmm::k_grouped_mm<F, TR, 128>), grid, block, 0, s, a, ntc);      \
+  } while (0)
   if (fmt == FMT_MXFP4) {
     if (trans) MXQ_GMM_LAUNCH(FMT_MXFP4, 1); else MXQ_GMM_LAUNCH(FMT_MXFP4, 0);
   } else {
