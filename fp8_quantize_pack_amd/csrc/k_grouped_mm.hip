@@ -311,13 +311,21 @@ void k_grouped_mm(Args a, int64_t ntiles_c) {
     store_stage<FMT, TRANS, BM>(st, As, Bs, tid);
     __syncthreads();
     if (r0 + BK < R) load_stage<FMT, TRANS, BM>(a, st, tid, e, m0, m1, c0, r0 + BK, R);
-    // backward: LLVM's MFMA-interleaving schedule (iglp strategy 1) measured
-    // 2-4% faster for MXFP4; for the forward product it is 27% slower
-    if constexpr (TRANS == 1) __builtin_amdgcn_iglp_opt(1);
+    // backward, 128-row tiles: LLVM's MFMA-interleaving schedule (iglp
+    // strategy 1) measured 2-4% faster for MXFP4; for the forward product it
+    // is 27% slower.  With 256-row tiles the backward runs 1-3% faster without
+    // it (MXFP4 291 against 300 us on the expert shapes).
+#ifndef MXQ_GMM_IGLP_256
+#define MXQ_GMM_IGLP_256 0
+#endif
+#ifndef MXQ_GMM_PRIO_256
+#define MXQ_GMM_PRIO_256 1
+#endif
+    if constexpr (TRANS == 1 && (BM == 128 || MXQ_GMM_IGLP_256)) __builtin_amdgcn_iglp_opt(1);
     // MXFP4: waves in their MFMA phase take issue priority over those loading,
     // dequantizing and storing the next tile (2.5-4% faster both ways); NVFP4's
     // heavier dequantization needs the issue slots (3% slower backward)
-    if constexpr (FMT == FMT_MXFP4) __builtin_amdgcn_s_setprio(1);
+    if constexpr (FMT == FMT_MXFP4 && (BM == 128 || MXQ_GMM_PRIO_256)) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       bf16x8 af[MT], bfr[2];
@@ -339,7 +347,7 @@ void k_grouped_mm(Args a, int64_t ntiles_c) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if constexpr (FMT == FMT_MXFP4) __builtin_amdgcn_s_setprio(0);
+    if constexpr (FMT == FMT_MXFP4 && (BM == 128 || MXQ_GMM_PRIO_256)) __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
 
