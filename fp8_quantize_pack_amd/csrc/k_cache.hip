@@ -67,15 +67,17 @@ __device__ __forceinline__ void cache_chunk(const Raw8<DT>& raw, bool ok, void* 
     } else {
       const double rs = 1.0 / (double)gs.s;     // sigma: an e4m3 value
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f[i] * rs));
+      for (int i = 0; i < 8; ++i) q[i] = half_down_for_rne((float)((double)f[i] * rs));
       cvt_scale = 1.0f;
     }
     // A midpoint tie is a float32 subnormal only under an mxfp4 scale
     // below 2^-124; waves holding one take the stochastic-rounding
     // converts, which need no tie-down step.
     const bool tiny = (FMT == FMT_MXFP4) && __any(gs.s < 0x1p-124f);
-    const uint32_t w = e2m1_canonical_zeros(__builtin_expect(tiny, 0) ? e2m1_pack8_hw(q, cvt_scale)
-                                                                       : e2m1_pack8_rne(q, cvt_scale));
+    const uint32_t w = e2m1_canonical_zeros(
+        __builtin_expect(tiny, 0) ? e2m1_pack8_hw(q, cvt_scale)
+        : FMT == FMT_MXFP4        ? e2m1_pack8_rne(q, cvt_scale)
+                                  : e2m1_pack8_even(q, cvt_scale));
     if constexpr (FMT == FMT_MXFP4 && DT == DT_BF16) {
       if (ok) stream_st(e2m1_unpack8_bf16_hw(w, gs.s), reinterpret_cast<u32x4*>(y) + c);
       return;

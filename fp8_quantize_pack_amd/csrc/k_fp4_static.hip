@@ -28,7 +28,8 @@
 // 1 / s' (hardware reciprocal, two Newton steps) rounded to float32: x has at
 // most 24 significant bits and s' 24, so the e2m1 decisions of that product
 // equal those of the float32 quotient (see nvfp4_quant8 in mxq_device.h);
-// then ceil22 and the round-half-down converter as in the NVFP4 kernels.
+// then the round-to-nearest-even converter, made to round half down by a
+// one-unit step on the operands that need it (half_down_for_rne).
 #include "mxq_kernel_common.h"
 #include "mxq_launch.h"
 
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(64 * kStWaves) void k_fp4_static_qdq(
       float f[8];
       unpack8<DT>(r[u], f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = ceil22((float)((double)f[i] * rs));
-      const uint32_t w = e2m1_canonical_zeros(e2m1_pack8_rne(f, 1.0f));
+      for (int i = 0; i < 8; ++i) f[i] = half_down_for_rne((float)((double)f[i] * rs));
+      const uint32_t w = e2m1_canonical_zeros(e2m1_pack8_even(f, 1.0f));
       float o[8];
       e2m1_unpack8_f32_hw(w, 1.0f, o);
 #pragma unroll

@@ -337,15 +337,15 @@ __device__ __forceinline__ void kv_quant_tile(const KvTile<DT>& t, const KvGeom&
   a1 = bitsf(max(fbits(a1), pair_swap(fbits(a1))));
   uint32_t sb;
   const double mine = nv_block_recip(odd ? a1 : a0, g_m, rg_m, sb);
-  const double other = pair_swap(mine);
-  const double r0 = odd ? other : mine, r1 = odd ? mine : other;
+  // chunk 0 lies in the even lane's block, chunk 1 in the odd lane's
+  const double r0 = pair_lane<kQuadEven>(mine), r1 = pair_lane<kQuadOdd>(mine);
   float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f0[i] * r0));
-  const uint32_t w0 = e2m1_pack8_rne(q, 1.0f);
+  for (int i = 0; i < 8; ++i) q[i] = nv_quotient(f0[i], r0);
+  const uint32_t w0 = e2m1_pack8_even(q, 1.0f);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = ceil22((float)((double)f1[i] * r1));
-  const uint32_t w1 = e2m1_pack8_rne(q, 1.0f);
+  for (int i = 0; i < 8; ++i) q[i] = nv_quotient(f1[i], r1);
+  const uint32_t w1 = e2m1_pack8_even(q, 1.0f);
   const int64_t cm = odd ? c + 64 : c;                // chunk of this lane's block
   const int64_t row = tile * R + lane / L;
   if (FULL || c < geo.nchunks) stream_st(w0, packed + c);

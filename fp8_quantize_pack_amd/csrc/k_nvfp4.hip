@@ -88,7 +88,7 @@ __device__ __forceinline__ void seg_quant(const SegChunks<DT>& c, const NvSegGeo
   uint32_t sb;
   const float a = amax_from_bits<DT>(odd ? p1 : p0);
   const double mine = NORMAL ? nv_block_recip_normal(a, g, rg, sb) : nv_block_recip(a, g, rg, sb);
-  const double other = pair_swap(mine);
+  const double other = pair_lane<kQuadSwap>(mine);
   const uint32_t w0 = nv_codes8<DT>(c.c0, odd ? other : mine);
   const uint32_t w1 = nv_codes8<DT>(c.c1, odd ? mine : other);
   const int64_t ch0 = (int64_t)seg * 128 + lane;

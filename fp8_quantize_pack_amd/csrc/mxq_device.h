@@ -92,6 +92,24 @@ MXQ_HD uint32_t e2m1_mag_f32(float q) {
 // operand that it aligns into the e2m1 subnormal range.)
 MXQ_HD float ceil22(float q) { return bitsf((fbits(q) + 3u) & ~3u); }
 
+// Operand for a round-to-nearest-even e2m1 conversion (scale 1, or a power of
+// two that keeps the midpoints normal) that is to round half down instead,
+// for any float32 q.  Ties to even already go down at the midpoints 0.25,
+// 1.25, 2.5 and 5 (their lower neighbour has the even code) and go up at
+// 0.75, 1.75 and 3.5 -- exactly the midpoints whose significand has bit 22
+// set (0.25 has none of its fraction bits set, the other three bit 21 only).
+// Taking one unit in the last place off every operand with that bit set
+// moves an operand that sits on one of those three just below it, and the
+// operand one unit above lands on the midpoint, which still rounds up.  A
+// one-unit step can carry an operand across a midpoint only from the
+// midpoint itself, so no other decision changes.  Zeros (bit 22 clear),
+// infinities (likewise) and subnormals (far below 0.25) keep their codes, and
+// the sign is untouched.
+MXQ_HD float half_down_for_rne(float q) {
+  const uint32_t u = fbits(q);
+  return bitsf(u - ((u >> 22) & 1u));
+}
+
 // 2 * e2m1 magnitude for code 0..7: 0 1 2 3 4 6 8 12 (an integer).
 MXQ_HD uint32_t e2m1_twice_mag(uint32_t c) {
   return (uint32_t)((0x0C08060403020100ull >> (8 * (c & 7))) & 0xFF);
@@ -133,9 +151,12 @@ MXQ_HD uint32_t e4m3_encode_pos(float u) {
 // on every float32 of that range; on the host e4m3_encode_pos_v itself.
 MXQ_HD uint32_t e4m3_encode_clamped(float u, float* value) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t b = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, u, 0, false) & 0xFFu;
-  *value = __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
-  return b;
+  // Both bytes of the low half take the code and the high half keeps the old
+  // operand (u's own bits, which saves zeroing a register); the decode reads
+  // byte 0 only.
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(u, u, (int)fbits(u), false);
+  *value = __builtin_amdgcn_cvt_f32_fp8(w, 0);
+  return (uint32_t)w & 0xFFu;
 #else
   return e4m3_encode_pos_v(u, value);
 #endif

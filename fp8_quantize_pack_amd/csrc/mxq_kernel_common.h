@@ -239,6 +239,16 @@ __device__ __forceinline__ uint32_t e2m1_pack8_rne(const float f[8], float scale
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6] * kTieDown, f[7] * kTieDown, scale, 3);
 }
 
+// The converter's own rounding, to nearest with ties to even, chained the same
+// way.  With operands passed through half_down_for_rne it rounds half down on
+// every float32, whatever its number of significant bits.
+__device__ __forceinline__ uint32_t e2m1_pack8_even(const float f[8], float scale) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(fbits(f[0]), f[0], f[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], scale, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], scale, 3);
+}
+
 // Clear the sign bit of every zero-magnitude nibble (code 8 -> 0), so that it
 // decodes to +0.0 as the e2m1 table prescribes.
 __device__ __forceinline__ uint32_t e2m1_canonical_zeros(uint32_t w) {

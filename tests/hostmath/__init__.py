@@ -21,7 +21,7 @@ _lib = None
 def build():
     tmp = LIB + ".tmp"
     subprocess.run([CXX, "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math",
-                    "-fPIC", "-shared", "-I", os.path.dirname(HDR), "-o", tmp, SRC],
+                    "-fPIC", "-shared", "-pthread", "-I", os.path.dirname(HDR), "-o", tmp, SRC],
                    check=True)
     os.replace(tmp, LIB)
 
@@ -45,6 +45,10 @@ def lib():
         L.hm_nv_division_stress.restype = i64
         L.hm_ceil22_check.argtypes = []
         L.hm_ceil22_check.restype = i64
+        L.hm_half_down_check.argtypes = []
+        L.hm_half_down_check.restype = i64
+        L.hm_rne_model_check.argtypes = []
+        L.hm_rne_model_check.restype = i64
         _lib = L
     return _lib
 

@@ -8,6 +8,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <thread>
+#include <vector>
+
 #include "mxq_device.h"
 
 using namespace mxq;
@@ -160,6 +163,69 @@ extern "C" int64_t hm_nv_division_stress(int64_t n, uint64_t seed, int wide) {
     const float u = (float)((double)div6_rn(fabsf(x)) * (1.0 / (double)g));
     if (fbits(u) != fbits(u_ref) && u_ref >= 1.17549435e-38f) ++bad;
   }
+  return bad;
+}
+
+// Model of the gfx950 fp4 converter's rounding at scale 1 (measured on the
+// chip: exact round to nearest, ties to the even code, saturating at 6):
+// the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 to |q|, on a tie the one whose
+// code is even.  Written from that definition, independently of
+// e2m1_mag_f32.
+static uint32_t e2m1_mag_rne_model(float q) {
+  static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double a = fabs((double)q);
+  if (a >= 6.0) return 7;                      // saturation, infinities included
+  uint32_t best = 0;
+  for (uint32_t c = 1; c < 8; ++c) {
+    const double dc = fabs(a - grid[c]), db = fabs(a - grid[best]);
+    if (dc < db || (dc == db && (c & 1u) == 0)) best = c;
+  }
+  return best;
+}
+
+// Every float32 magnitude below 16, both signs, and the infinities: the
+// converter's ties-to-even rounding of half_down_for_rne(q) gives the
+// round-half-down code of q (e2m1_mag_f32), with the sign of q.  Returns the
+// number of disagreements.
+static int64_t half_down_range(uint32_t b0, uint32_t b1) {
+  int64_t bad = 0;
+  for (uint32_t b = b0; b < b1; ++b) {
+    for (uint32_t s = 0; s < 2; ++s) {
+      const float q = bitsf(b | (s << 31));
+      const float v = half_down_for_rne(q);
+      if (e2m1_mag_rne_model(v) != e2m1_mag_f32(fabsf(q))) ++bad;
+      if ((fbits(v) ^ fbits(q)) >> 31) ++bad;
+    }
+  }
+  return bad;
+}
+
+extern "C" int64_t hm_half_down_check(void) {
+  constexpr uint32_t kEnd = 0x41800001u;       // every magnitude up to 16
+  constexpr int kParts = 8;
+  int64_t part[kParts] = {};
+  std::vector<std::thread> pool;
+  for (int t = 0; t < kParts; ++t)
+    pool.emplace_back([&part, t] {
+      part[t] = half_down_range((uint32_t)((uint64_t)kEnd * t / kParts),
+                                (uint32_t)((uint64_t)kEnd * (t + 1) / kParts));
+    });
+  int64_t bad = 0;
+  for (int t = 0; t < kParts; ++t) { pool[t].join(); bad += part[t]; }
+  if (e2m1_mag_rne_model(half_down_for_rne(bitsf(0x7F800000u))) != 7u) ++bad;
+  if (e2m1_mag_rne_model(half_down_for_rne(bitsf(0xFF800000u))) != 7u) ++bad;
+  return bad;
+}
+
+// The model above against the definition it states, on the grid values and
+// midpoints themselves: returns the number of mismatches.
+extern "C" int64_t hm_rne_model_check(void) {
+  static const float pts[] = {0.0f, 0.25f, 0.5f, 0.75f, 1.0f, 1.25f, 1.5f, 1.75f,
+                              2.0f, 2.5f, 3.0f, 3.5f, 4.0f, 5.0f, 6.0f, 7.0f, 100.0f};
+  static const uint32_t want[] = {0, 0, 1, 2, 2, 2, 3, 4, 4, 4, 5, 6, 6, 6, 7, 7, 7};
+  int64_t bad = 0;
+  for (int i = 0; i < (int)(sizeof(pts) / sizeof(pts[0])); ++i)
+    if (e2m1_mag_rne_model(pts[i]) != want[i]) ++bad;
   return bad;
 }
 

@@ -259,3 +259,16 @@ def test_nvfp4_binary64_division_shortcut_stress(wide):
 def test_rounding_up_to_22_bits_keeps_every_e2m1_decision():
     """Exhaustive over all float32 magnitudes below 16 (about 1.1e9 values)."""
     assert hm.lib().hm_ceil22_check() == 0
+
+
+def test_ties_to_even_model_on_grid_and_midpoints():
+    """The host model of the fp4 converter (nearest, ties to the even code,
+    saturating at 6) on every e2m1 value and midpoint."""
+    assert hm.lib().hm_rne_model_check() == 0
+
+
+def test_half_down_operand_step_keeps_every_e2m1_decision():
+    """Exhaustive over all float32 magnitudes below 16, both signs (about
+    2.2e9 values): ties-to-even rounding of half_down_for_rne(q) equals the
+    round-half-down code of q, sign kept."""
+    assert hm.lib().hm_half_down_check() == 0
