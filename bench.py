@@ -223,8 +223,8 @@ def main():
             for _ in range(CACHE_CYCLES) for xi, yo in cache_sets[c]]
     reps = max(args.steps, 5)
     ops = {}
-    op_times = time_graphs_interleaved(torch, {n: [fn for _, fn in l] for n, l in op_launches.items()},
-                                       reps)
+    op_graphs = capture_graphs(torch, {n: [fn for _, fn in l] for n, l in op_launches.items()})
+    op_times = time_graphs_interleaved(torch, op_graphs, reps)
     for name, launches in op_launches.items():
         t = op_times[name]
         nb = sum(b for b, _ in launches)
@@ -236,12 +236,17 @@ def main():
                      "GBps": round(nb / t / 1e9, 1), "frac_of_peak": round(nb / t / 1e9 / PEAK_HBM_GBPS, 4),
                      "event_pair_avg_us": round(ms_ev * 1e3 / n_ev, 2),
                      "step_us": round(t / len(launches) * per_step_launches * 1e6, 1)}
-    del cache_sets
-    progress("per-operation graphs timed")
     fp4 = [n for n in ops if not n.startswith("cache")]
     fp4_bytes = sum(b for n, b, _ in plan if n in fp4)
     fp4_s = sum(ops[n]["step_us"] for n in fp4) * 1e-6
     dom = max(ops, key=lambda n: ops[n]["step_us"])
+    # the dominant operation's launch time straight after each sweep
+    # operation: the chip's clock and power state carry over from one
+    # kernel to the next, and the sweep kernels differ in VALU load
+    after = time_after(torch, op_graphs, dom, fp4, reps)
+    by_pred = {p: round(t / len(op_launches[dom]) * 1e6, 2) for p, t in after.items()}
+    del op_graphs, cache_sets
+    progress("per-operation graphs timed")
     src_hash = kernel_source_hash()
     traffic = measured_traffic(dom, src_hash)
 
@@ -252,7 +257,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic,
                 "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"],
-                "avg_launch_us": ops[dom]["avg_launch_us"]}
+                "avg_launch_us": ops[dom]["avg_launch_us"],
+                "avg_launch_us_after": by_pred}
     if ref:
         cp = ref["copy"]["sweep_chunk"]
         roofline["copy_GBps"] = cp["GBps"]
@@ -311,12 +317,9 @@ CACHE_SETS = 8
 CACHE_CYCLES = 4     # passes over the rotating sets in one timed graph
 
 
-def time_graphs_interleaved(torch, fns_by_name, reps):
-    """Seconds for one pass over each list of launches: each list captured
-    once as a HIP graph; the graphs are replayed in turn, `reps` rounds, each
-    replay between two HIP events on the launch stream (so every operation is
-    timed among the others, as in the step, rather than after a long run of
-    itself); the mean over the rounds."""
+def capture_graphs(torch, fns_by_name):
+    """Each list of launches captured once as a HIP graph (after one eager
+    pass) and replayed once."""
     graphs = {}
     for name, fns in fns_by_name.items():
         for f in fns:
@@ -329,6 +332,14 @@ def time_graphs_interleaved(torch, fns_by_name, reps):
         g.replay()
         graphs[name] = g
     torch.cuda.synchronize()
+    return graphs
+
+
+def time_graphs_interleaved(torch, graphs, reps):
+    """Seconds for one replay of each graph: the graphs are replayed in turn,
+    `reps` rounds, each replay between two HIP events on the launch stream (so
+    every operation is timed among the others, as in the step, rather than
+    after a long run of itself); the mean over the rounds."""
     ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)] for n in graphs}
     for r in range(reps):
@@ -337,8 +348,24 @@ def time_graphs_interleaved(torch, fns_by_name, reps):
             g.replay()
             ev[n][r][1].record()
     torch.cuda.synchronize()
-    out = {n: sum(a.elapsed_time(b) for a, b in ev[n]) * 1e-3 / reps for n in graphs}
-    del graphs
+    return {n: sum(a.elapsed_time(b) for a, b in ev[n]) * 1e-3 / reps for n in graphs}
+
+
+def time_after(torch, graphs, target, preds, reps):
+    """Seconds for one replay of graphs[target] started straight after a
+    replay of graphs[p], for each p in preds (no synchronization in between;
+    `reps` pairs each, the mean)."""
+    out = {}
+    for p in preds:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            graphs[p].replay()
+            a.record()
+            graphs[target].replay()
+            b.record()
+        torch.cuda.synchronize()
+        out[p] = sum(a.elapsed_time(b) for a, b in ev) * 1e-3 / reps
     return out
 
 
