@@ -63,6 +63,11 @@ def parse():
                          "chunk (reads and writes CALIBRATION_BYTES) for HBM counter calibration")
     ap.add_argument("--no-ref", action="store_true",
                     help="skip the copy / read / write reference kernels")
+    ap.add_argument("--by-predecessor", action="store_true",
+                    help="also time the dominant operation's graph straight after each sweep "
+                         "operation's graph (roofline.avg_launch_us_after); off by default, so "
+                         "that a kernel trace of the default run holds the step's launches and "
+                         "the per-operation graphs only")
     return ap.parse_args()
 
 
@@ -243,8 +248,10 @@ def main():
     # the dominant operation's launch time straight after each sweep
     # operation: the chip's clock and power state carry over from one
     # kernel to the next, and the sweep kernels differ in VALU load
-    after = time_after(torch, op_graphs, dom, fp4, reps)
-    by_pred = {p: round(t / len(op_launches[dom]) * 1e6, 2) for p, t in after.items()}
+    by_pred = None
+    if args.by_predecessor:
+        after = time_after(torch, op_graphs, dom, fp4, reps)
+        by_pred = {p: round(t / len(op_launches[dom]) * 1e6, 2) for p, t in after.items()}
     del op_graphs, cache_sets
     progress("per-operation graphs timed")
     src_hash = kernel_source_hash()
@@ -257,8 +264,9 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic,
                 "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"],
-                "avg_launch_us": ops[dom]["avg_launch_us"],
-                "avg_launch_us_after": by_pred}
+                "avg_launch_us": ops[dom]["avg_launch_us"]}
+    if by_pred is not None:
+        roofline["avg_launch_us_after"] = by_pred
     if ref:
         cp = ref["copy"]["sweep_chunk"]
         roofline["copy_GBps"] = cp["GBps"]

@@ -50,10 +50,10 @@ BENCH_KERNELS = {
     "kv_head_amax": "mxq::k_kv_head_amax<1, true, 16>",
     "kv_quant": "mxq::k_kv_quant<1, true, 16>",
     "kv_pages_dequant": "mxq::k_kv_pages_dequant<1>",
-    "gemm_mxfp4_forward": "mxq::gmm::k_grouped_mm<1, 0, 128>",
-    "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1, 128>",
-    "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0, 128>",
-    "gemm_nvfp4_backward": "mxq::gmm::k_grouped_mm<2, 1, 128>",
+    "gemm_mxfp4_forward": "mxq::gmm::k_grouped_mm<1, 0, 256>",
+    "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1, 256>",
+    "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0, 256>",
+    "gemm_nvfp4_backward": "mxq::gmm::k_grouped_mm<2, 1, 256>",
     "ref_copy_u1": "(anonymous namespace)::k_copy<1>",
     "ref_copy_u2": "(anonymous namespace)::k_copy<2>",
     "ref_copy_u4": "(anonymous namespace)::k_copy<4>",
@@ -72,7 +72,7 @@ CALIBRATION_MARK = "k_copy<2>"
 # Host-side argument checking does not change a kernel's traffic.
 CODEC_SOURCES = ("mxq_device.h", "mxq_kernel_common.h", "mxq_nvfp4_common.h",
                  "k_mxfp4.hip", "k_nvfp4.hip", "k_cache.hip",
-                 "k_mxfp8.hip", "k_fp4_static.hip", "k_kv.hip")
+                 "k_mxfp8.hip", "k_fp4_static.hip", "k_kv.hip", "k_grouped_mm.hip")
 
 
 def code_tokens(text: str) -> str:
