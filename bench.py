@@ -245,13 +245,14 @@ def main():
     fp4_bytes = sum(b for n, b, _ in plan if n in fp4)
     fp4_s = sum(ops[n]["step_us"] for n in fp4) * 1e-6
     dom = max(ops, key=lambda n: ops[n]["step_us"])
-    # the dominant operation's launch time straight after each sweep
-    # operation: the chip's clock and power state carry over from one
-    # kernel to the next, and the sweep kernels differ in VALU load
+    # on request, the dominant operation's launch time straight after each
+    # sweep operation (it depends on the predecessor), and the shader clock
+    # read right after each of them
     by_pred = None
     if args.by_predecessor:
         after = time_after(torch, op_graphs, dom, fp4, reps)
         by_pred = {p: round(t / len(op_launches[dom]) * 1e6, 2) for p, t in after.items()}
+        clock_after = shader_clock_after(torch, op_graphs, fp4, reps, dev)
     del op_graphs, cache_sets
     progress("per-operation graphs timed")
     src_hash = kernel_source_hash()
@@ -267,6 +268,7 @@ def main():
                 "avg_launch_us": ops[dom]["avg_launch_us"]}
     if by_pred is not None:
         roofline["avg_launch_us_after"] = by_pred
+        roofline["shader_clock_MHz_after"] = clock_after
     if ref:
         cp = ref["copy"]["sweep_chunk"]
         roofline["copy_GBps"] = cp["GBps"]
@@ -375,6 +377,24 @@ def time_after(torch, graphs, target, preds, reps):
         torch.cuda.synchronize()
         out[p] = sum(a.elapsed_time(b) for a, b in ev) * 1e-3 / reps
     return out
+
+
+def shader_clock_after(torch, graphs, preds, reps, dev):
+    """Mean shader clock (MHz) read by the clock probe of libmxq_roofline
+    launched straight after a replay of graphs[p], for each p in preds
+    (`reps` pairs each)."""
+    from fp8_quantize_pack_amd import roofline as rl
+    out = torch.zeros(2 * 256, dtype=torch.int64, device=dev)
+    res = {}
+    for p in preds:
+        vals = []
+        for _ in range(reps):
+            graphs[p].replay()
+            rl.clock(out, iters=4096)
+            torch.cuda.synchronize()
+            vals.append(rl.clock_mhz(out))
+        res[p] = round(sum(vals) / len(vals), 1)
+    return res
 
 
 def time_graph(torch, fns, reps):

@@ -1,6 +1,6 @@
 // k_roofline_ref.hip -- plain streaming kernels that give the practical HBM
 // ceiling the codec kernels are compared with: copy (read + write), read only
-// and write only.  They move 16-byte chunks with the same non-temporal vector
+// and write only; and a shader clock probe.  They move 16-byte chunks with the same non-temporal vector
 // accesses and the same wave-tile mapping as the codec kernels (in step u of
 // a tile lane l owns chunk tile * U * 64 + u * 64 + l, so every wave
 // instruction touches one contiguous 1 KiB range; four waves per workgroup,
@@ -80,6 +80,24 @@ __global__ __launch_bounds__(64 * kWaves) void k_fill(v4u* __restrict__ dst, int
   }
 }
 
+// Shader clock probe: every workgroup (one wave) reads the shader cycle
+// counter (s_memtime) and the constant 100 MHz counter (s_memrealtime) around
+// a chain of `iters` dependent VALU operations; lane 0 stores both
+// differences, so that their ratio is the mean shader clock over the window.
+__global__ __launch_bounds__(64) void k_clock(uint64_t* __restrict__ out, int32_t iters) {
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  float v = (float)threadIdx.x;
+  for (int32_t i = 0; i < iters; ++i) v = __builtin_fmaf(v, 0.999f, 0.5f);
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  if (v == -1.0f) out[0] = 0;      // keeps the chain; v stays positive
+}
+
 int grid_for(int64_t ntiles) {
   const int64_t b = (ntiles + kWaves - 1) / kWaves;
   return (int)(b < kMaxBlocks ? (b > 0 ? b : 1) : kMaxBlocks);
@@ -134,6 +152,14 @@ int mxq_ref_fill(void* dst, int64_t bytes, uint32_t value, int32_t unroll,
   const int64_t n = bytes / 16, tiles = (n + unroll * kWave - 1) / (unroll * kWave);
   MXQ_REF_DISPATCH(k_fill, unroll, dim3(grid_for(tiles)), dim3(64 * kWaves), 0, stream,
                    static_cast<v4u*>(dst), n, tiles, value);
+  return hipGetLastError() == hipSuccess ? MXQ_REF_OK : MXQ_REF_E_LAUNCH;
+}
+
+int mxq_ref_clock(uint64_t* out, int32_t blocks, int32_t iters, hipStream_t stream) {
+  if (!out) return MXQ_REF_E_NULL;
+  if (reinterpret_cast<uintptr_t>(out) % 8) return MXQ_REF_E_ALIGN;
+  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 24)) return MXQ_REF_E_SHAPE;
+  hipLaunchKernelGGL(k_clock, dim3(blocks), dim3(64), 0, stream, out, iters);
   return hipGetLastError() == hipSuccess ? MXQ_REF_OK : MXQ_REF_E_LAUNCH;
 }
 

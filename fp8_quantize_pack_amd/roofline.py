@@ -25,7 +25,8 @@ def lib() -> ctypes.CDLL:
         L.mxq_ref_copy.argtypes = [vp, vp, i64, i32, vp]
         L.mxq_ref_read.argtypes = [vp, i64, i32, u32, vp, vp]
         L.mxq_ref_fill.argtypes = [vp, i64, u32, i32, vp]
-        for f in ("mxq_ref_copy", "mxq_ref_read", "mxq_ref_fill"):
+        L.mxq_ref_clock.argtypes = [vp, i32, i32, vp]
+        for f in ("mxq_ref_copy", "mxq_ref_read", "mxq_ref_fill", "mxq_ref_clock"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -61,3 +62,18 @@ def read(src: torch.Tensor, sink: torch.Tensor, unroll: int = 2, magic: int = 0x
 def fill(dst: torch.Tensor, value: int = 0, unroll: int = 2) -> None:
     _ok(lib().mxq_ref_fill(dst.data_ptr(), _nbytes(dst), value, unroll, _stream(dst)),
         "mxq_ref_fill")
+
+
+def clock(out: torch.Tensor, iters: int = 4096) -> None:
+    """Launch the shader clock probe: out is an int64 GPU tensor of 2 * blocks
+    values (blocks workgroups of one wave); read it with clock_mhz."""
+    if out.dtype != torch.int64 or out.numel() % 2 or out.numel() == 0:
+        raise ValueError("clock probe output: a non-empty int64 tensor of 2 * blocks values")
+    _nbytes(out)
+    _ok(lib().mxq_ref_clock(out.data_ptr(), out.numel() // 2, iters, _stream(out)), "mxq_ref_clock")
+
+
+def clock_mhz(out: torch.Tensor) -> float:
+    """Mean shader clock in MHz from a clock probe's output (host read)."""
+    v = out.view(-1, 2).cpu().double()
+    return float(v[:, 0].sum() / v[:, 1].sum() * 100.0)

@@ -47,6 +47,15 @@ int mxq_ref_read(const void* src, int64_t bytes, int32_t unroll, uint32_t magic,
 int mxq_ref_fill(void* dst, int64_t bytes, uint32_t value, int32_t unroll,
                  hipStream_t stream);
 
+/* Shader clock probe: `blocks` workgroups of one wave each read the shader
+ * cycle counter and the constant 100 MHz counter around a chain of `iters`
+ * dependent VALU operations and store, per workgroup, the two differences:
+ * out[2 b] = shader cycles, out[2 b + 1] = 100 MHz ticks (out holds 2 * blocks
+ * 8-byte-aligned values).  sum(cycles) / sum(ticks) * 100 is the mean shader
+ * clock in MHz over the window.  blocks in [1, 65536], iters in [1, 2^24],
+ * else MXQ_REF_E_SHAPE. */
+int mxq_ref_clock(uint64_t* out, int32_t blocks, int32_t iters, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

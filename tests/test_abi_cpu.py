@@ -296,7 +296,7 @@ def test_roofline_library_exports_and_validation():
     from fp8_quantize_pack_amd import roofline
     L = roofline.lib()
     names = _declared_functions("mxq_roofline.h")
-    assert names == ["mxq_ref_copy", "mxq_ref_fill", "mxq_ref_read"]
+    assert names == ["mxq_ref_clock", "mxq_ref_copy", "mxq_ref_fill", "mxq_ref_read"]
     for n in names:
         assert hasattr(L, n), n
     assert L.mxq_ref_copy(FAKE, FAKE, 24, 2, None) == 2          # not a multiple of 16
@@ -309,6 +309,12 @@ def test_roofline_library_exports_and_validation():
     assert L.mxq_ref_read(FAKE + 4, 64, 2, 0, FAKE, None) == 9
     assert L.mxq_ref_fill(FAKE, 40, 0, 2, None) == 2
     assert L.mxq_ref_fill(FAKE, 64, 0, 16, None) == 5
+    assert L.mxq_ref_clock(None, 4, 16, None) == 1
+    assert L.mxq_ref_clock(FAKE + 4, 4, 16, None) == 9
+    assert L.mxq_ref_clock(FAKE, 0, 16, None) == 2
+    assert L.mxq_ref_clock(FAKE, 65537, 16, None) == 2
+    assert L.mxq_ref_clock(FAKE, 4, 0, None) == 2
+    assert L.mxq_ref_clock(FAKE, 4, (1 << 24) + 1, None) == 2
 
 
 def test_noalloc_validation(L):
