@@ -272,6 +272,42 @@ def summarize_counters(csvs, command: str, elements: dict) -> str:
     return "\n".join(out) + "\n"
 
 
+def summarize_runs(trace_csv: str, command: str, op: str, length: int) -> str:
+    """Runs of `length` back-to-back dispatches of one bench op (a graph
+    replay of its chunk launches) in a per-dispatch kernel trace, each with
+    the op of the dispatches just before it, the idle gap before the run and
+    its per-dispatch durations: how an op's time depends on its predecessor,
+    and whether that holds for the whole run or only its first launch."""
+    inv = {v: k for k, v in BENCH_KERNELS.items()}
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = short_name(r["Kernel_Name"])
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), inv.get(name, name)))
+    rows.sort()
+    runs, i = [], 0
+    while i < len(rows):
+        j = i
+        while j < len(rows) and rows[j][2] == rows[i][2]:
+            j += 1
+        runs.append((rows[i][2], i, j))
+        i = j
+    out = [f"# rocprofv3 kernel trace (one MI355X): runs of {length} back-to-back {op} dispatches and "
+           "the op just before each run",
+           f"# command: {command}",
+           f"# kernel_source_hash: {kernel_source_hash()}",
+           "# durations in microseconds; gap = idle time between the predecessor's last dispatch and the run",
+           f"{'predecessor':28s} {'gap_us':>7s} {'first':>8s} {'middle_mean':>11s} {'last':>7s} {'run_sum':>8s}"]
+    for k, (name, i, j) in enumerate(runs):
+        if name != op or j - i != length or k == 0:
+            continue
+        d = [(rows[t][1] - rows[t][0]) / 1e3 for t in range(i, j)]
+        gap = (rows[i][0] - rows[i - 1][1]) / 1e3
+        mid = sum(d[1:-1]) / max(1, len(d) - 2)
+        out.append(f"{runs[k - 1][0][:28]:28s} {gap:7.1f} {d[0]:8.1f} {mid:11.1f} {d[-1]:7.1f} {sum(d):8.1f}")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -289,8 +325,13 @@ def main():
     q.add_argument("out"); q.add_argument("csvs", nargs="+")
     q.add_argument("--command", required=True)
     q.add_argument("--elements", default="", help="op=elements,... elements per launch")
+    r = sub.add_parser("runs")
+    r.add_argument("trace_csv"); r.add_argument("out"); r.add_argument("--command", required=True)
+    r.add_argument("--op", required=True); r.add_argument("--length", type=int, default=8)
     a = ap.parse_args()
-    if a.what == "trace":
+    if a.what == "runs":
+        txt = summarize_runs(a.trace_csv, a.command, a.op, a.length)
+    elif a.what == "trace":
         txt = summarize_trace(a.stats_csv, a.command)
         if a.dispatches:
             txt += "\n" + summarize_trace_dispatches(a.dispatches, a.command)

@@ -57,3 +57,25 @@ def test_code_tokens_ignore_comments_and_layout_only():
     assert prof.code_tokens("int x = 1;") != prof.code_tokens("int x = 2;")
     assert "// not a comment" in prof.code_tokens(a)
 
+
+
+def test_runs_table_groups_back_to_back_dispatches(tmp_path):
+    path = tmp_path / "trace.csv"
+    nv = "void mxq::k_nvfp4_quant_seg<1, 7, 1, true>(void const*, mxq::NvSegGeom)"
+    mx = "void mxq::k_mxfp4_dequant<1>(unsigned int const*, unsigned char const*)"
+    rows, t = [], 0
+    for name, n, dur in ((mx, 2, 100), (nv, 3, 200), (mx, 1, 100), (nv, 2, 50), (nv, 0, 0)):
+        for _ in range(n):
+            rows.append((name, t, t + dur * 1000))
+            t += dur * 1000 + 5000
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, a, b in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": a, "End_Timestamp": b})
+    txt = prof.summarize_runs(str(path), "cmd", "nvfp4_quant", 3)
+    lines = [l for l in txt.splitlines() if not l.startswith("#") and not l.startswith("predecessor")]
+    # only the 3-dispatch run counts; its predecessor is the MXFP4 dequantizer, 5 us before it
+    assert len(lines) == 1
+    f = lines[0].split()
+    assert f[0] == "mxfp4_dequant" and f[1] == "5.0" and f[2] == "200.0" and f[5] == "600.0"
