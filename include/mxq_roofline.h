@@ -1,7 +1,8 @@
 /*
  * mxq_roofline.h -- C ABI of libmxq_roofline: plain streaming kernels that
- * measure the practical HBM ceiling of one MI355X (gfx950), against which the
- * codec kernels of libmxq are judged.  Not part of the codec: these calls
+ * measure the practical HBM ceiling of one MI355X (gfx950), with which the
+ * codec kernels of libmxq are compared, and a shader clock probe.  Not part
+ * of the codec: these calls
  * compute nothing the source pages define; they move bytes with the same
  * 16-byte non-temporal vector accesses and the same wave-tile mapping as the
  * codec's streaming kernels (every wave instruction touches one contiguous
