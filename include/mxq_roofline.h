@@ -2,8 +2,8 @@
  * mxq_roofline.h -- C ABI of libmxq_roofline: plain streaming kernels that
  * measure the practical HBM ceiling of one MI355X (gfx950), with which the
  * codec kernels of libmxq are compared, and a shader clock probe.  Not part
- * of the codec: these calls
- * compute nothing the source pages define; they move bytes with the same
+ * of the codec.  The streaming calls compute nothing the source pages
+ * define; they move bytes with the same
  * 16-byte non-temporal vector accesses and the same wave-tile mapping as the
  * codec's streaming kernels (every wave instruction touches one contiguous
  * 1 KiB range; four waves per workgroup, one tile of `unroll` x 64 chunks per
