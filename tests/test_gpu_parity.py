@@ -303,7 +303,7 @@ def test_nvfp4_sweep_specials():
 # 7168 and 16400 columns take the row kernels with 7 and 5 segments per wave
 # (one and four waves a row), which launch at four workgroups per CU
 @pytest.mark.parametrize("K", [256, 2064, 7168, 16400])
-@pytest.mark.parametrize("kind", ["pow2", "random", "scalar", "edge", "negative", "bounds"])
+@pytest.mark.parametrize("kind", ["pow2", "random", "scalar", "edge", "negative", "bounds", "overflow"])
 def test_nvfp4_given_scales(kind, K):
     say("nvfp4 given", kind, K)
     rng = np.random.default_rng(3)
@@ -323,6 +323,14 @@ def test_nvfp4_given_scales(kind, K):
         b = np.array([2.0 ** -100, 2.0 ** 100], np.float32)
         gv = torch.from_numpy(np.resize(np.concatenate(
             [b, np.nextafter(b, np.float32(0)), np.nextafter(b, np.float32(np.inf)), b * 2, b / 2]), R))
+    elif kind == "overflow":
+        # elements near the bfloat16 maximum under small row scales in the
+        # per-row fast range: x / (block scale * g) overflows float32 to
+        # +-inf (and the block scale clamps at 448), so every such code
+        # saturates, with its sign
+        x = (x.float() * 1e38).clamp(-3.3e38, 3.3e38).to(torch.bfloat16)
+        x[::7, ::5] = 1.0                              # ordinary values beside them
+        gv = torch.from_numpy(np.resize(np.array([2.0 ** -100, 1e-20, 1e-5, 3.0], np.float32), R))
     else:
         x[3] = 0
         gv = torch.from_numpy(np.resize(np.array([0.0, 1e-42, 1e30, np.inf, 2.0 ** -126, 3.0, 1e-20, 1e20],
