@@ -56,6 +56,18 @@ struct Args {
   int64_t T, E, N, K;
 };
 
+// float32 value of an e4m3fn byte: the magnitude through the hardware e4m3
+// converter (exact for every finite byte; NaN for the NaN byte 0x7F), the
+// sign set by hand (so that 0x80 is -0).  Finite bytes decode bit for bit as
+// e4m3_decode_any does; a NaN byte gives the hardware's NaN, and every output
+// the weights of its block reach is NaN whatever the payload.  Four
+// instructions and no case split (the software decode's conditionals compile
+// to branches).
+__device__ __forceinline__ float e4m3_decode_hw(uint32_t b) {
+  const uint32_t d = fbits(__builtin_amdgcn_cvt_f32_fp8((int)(b & 0x7Fu), 0));
+  return bitsf(d | ((b & 0x80u) << 24));
+}
+
 // Dequantized bf16 of 8 consecutive weights (one packed dword) in the
 // arithmetic of dequantize_mxfp4 / dequantize_nvfp4 with a bf16 output, up
 // to the sign of zero: code 8 stays -0 here (the dequantizers give +0).  The
@@ -69,7 +81,7 @@ __device__ __forceinline__ u32x4 deq8(uint32_t w, uint32_t sb, float g) {
     if (sb == 255u) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
     return o;
   } else {
-    const float sigma = e4m3_decode_any(sb);
+    const float sigma = e4m3_decode_hw(sb);
     float f[8];
     e2m1_unpack8_f32_hw(w, 1.0f, f);
 #pragma unroll
@@ -86,13 +98,60 @@ __device__ __forceinline__ uint32_t scale_at(const Args& a, int64_t row, int64_t
   return a.scales[row * (a.K / B) + k / B];
 }
 
+// Registers holding one reduction step of a thread's share of the weight tile.
+struct WStage {
+  u32x4 wv;                   // 32 packed codes of one weight row
+  uint32_t sb;                // MXFP4: the scale byte; NVFP4: the scale bytes
+                              // of the two 16-column halves, low byte first
+  float g;                    // NVFP4 row scale
+};
+
+template <int FMT, int TRANS>
+__device__ __forceinline__ void load_w(const Args& a, WStage& w, int tid, int64_t e, int64_t c0,
+                                       int64_t r0) {
+  int64_t row, k;
+  if constexpr (TRANS == 0) {
+    // W_e rows c0 .. c0+127, columns r0 .. r0+63: thread -> (row tid/2, half tid%2)
+    row = e * a.N + c0 + (tid >> 1);
+    k = r0 + (tid & 1) * 32;
+  } else {
+    // W_e rows r0 .. r0+63 (reduction), columns c0 .. c0+127: thread -> (row
+    // tid/4, quarter tid%4 of 32 columns); 4 lanes read each row's 64 bytes
+    row = e * a.N + r0 + (tid >> 2);
+    k = c0 + (tid & 3) * 32;
+  }
+  w.wv = *reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2);
+  if constexpr (FMT == FMT_MXFP4) {
+    w.sb = scale_at<FMT>(a, row, k);
+  } else {
+    // the two scale bytes are adjacent (k is a multiple of 32): one 16-bit
+    // load, so that no arithmetic joins two loads right after they issue
+    uint16_t pair;
+    __builtin_memcpy(&pair, a.scales + row * (a.K / 16) + k / 16, 2);
+    w.sb = pair;
+  }
+  w.g = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
+}
+
+template <int FMT, int TRANS>
+__device__ __forceinline__ void store_w(const WStage& w, uint16_t* Bs, int tid) {
+  const uint32_t v[4] = {w.wv.x, w.wv.y, w.wv.z, w.wv.w};
+  // forward: [output column][reduction] rows of the tile; backward: weight
+  // row n (reduction), output columns kq .. kq+31 stay a row of the tile and
+  // the MFMA operand is transposed on the way out of LDS
+  uint16_t* dst = TRANS == 0 ? Bs + (tid >> 1) * LDS_STRIDE + (tid & 1) * 32
+                             : Bs + (tid >> 2) * WT_STRIDE + (tid & 3) * 32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<u32x4*>(dst + 8 * j) =
+        deq8<FMT>(v[j], FMT == FMT_MXFP4 ? w.sb : (w.sb >> (8 * (j >> 1))) & 0xFFu, w.g);
+}
+
 // Registers holding one reduction step of both operands in flight.
 template <int BM>
 struct Stage {
   u32x4 av[BM / 32];          // BM / 32 x 8 activations
-  u32x4 wv;                   // 32 packed codes of one weight row
-  uint32_t sb[2];             // scale bytes of the two 16-column halves
-  float g[1];                 // NVFP4 row scale
+  WStage w;
 };
 
 template <int FMT, int TRANS, int BM>
@@ -107,24 +166,7 @@ __device__ __forceinline__ void load_stage(const Args& a, Stage<BM>& st, int tid
     st.av[i] = row < m1 ? *reinterpret_cast<const u32x4*>(a.x + row * R + r0 + (c & 7) * 8)
                         : u32x4{0u, 0u, 0u, 0u};
   }
-  if constexpr (TRANS == 0) {
-    // W_e rows c0 .. c0+127, columns r0 .. r0+63: thread -> (row tid/2, half tid%2)
-    const int64_t row = e * a.N + c0 + (tid >> 1);
-    const int64_t k = r0 + (tid & 1) * 32;
-    st.wv = *reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2);
-    st.sb[0] = scale_at<FMT>(a, row, k);
-    st.sb[1] = (FMT == FMT_MXFP4) ? st.sb[0] : scale_at<FMT>(a, row, k + 16);
-    st.g[0] = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
-  } else {
-    // W_e rows r0 .. r0+63 (reduction), columns c0 .. c0+127: thread -> (row
-    // tid/4, quarter tid%4 of 32 columns); 4 lanes read each row's 64 bytes
-    const int64_t row = e * a.N + r0 + (tid >> 2);
-    const int64_t k = c0 + (tid & 3) * 32;
-    st.wv = *reinterpret_cast<const u32x4*>(a.packed + row * (a.K / 2) + k / 2);
-    st.sb[0] = scale_at<FMT>(a, row, k);
-    st.sb[1] = (FMT == FMT_MXFP4) ? st.sb[0] : scale_at<FMT>(a, row, k + 16);
-    st.g[0] = (FMT == FMT_NVFP4) ? a.row_scale[row] : 1.0f;
-  }
+  load_w<FMT, TRANS>(a, st.w, tid, e, c0, r0);
 }
 
 template <int FMT, int TRANS, int BM>
@@ -134,21 +176,7 @@ __device__ __forceinline__ void store_stage(const Stage<BM>& st, uint16_t* As, u
     const int c = tid + THREADS * i;
     *reinterpret_cast<u32x4*>(As + (c >> 3) * LDS_STRIDE + (c & 7) * 8) = st.av[i];
   }
-  const uint32_t w[4] = {st.wv.x, st.wv.y, st.wv.z, st.wv.w};
-  if constexpr (TRANS == 0) {
-    uint16_t* dst = Bs + (tid >> 1) * LDS_STRIDE + (tid & 1) * 32;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(dst + 8 * j) = deq8<FMT>(w[j], st.sb[j >> 1], st.g[0]);
-  } else {
-    // backward: weight row n (reduction), output columns kq .. kq+31 stay a
-    // row of the tile; the MFMA operand is transposed on the way out of LDS
-    const int n = tid >> 2, kq = (tid & 3) * 32;
-    uint16_t* dst = Bs + n * WT_STRIDE + kq;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(dst + 8 * j) = deq8<FMT>(w[j], st.sb[j >> 1], st.g[0]);
-  }
+  store_w<FMT, TRANS>(st.w, Bs, tid);
 }
 
 // Backward B operand of v_mfma_f32_32x32x16_bf16 from the row-major weight

@@ -202,3 +202,65 @@ def test_grouped_mm_one_hot_reproduces_dequantized_weights(fmt, transpose, shape
     yb, rb = y.view(torch.int16), ref.view(torch.int16)
     bad = (yb != rb) & ~zero
     assert not bad.any(), f"{fmt}: {int(bad.sum())} weights differ, first at {bad.nonzero()[:4].tolist()}"
+
+
+# ------------------------------------------------------------------ 256-row tiles, whole outputs
+
+@pytest.mark.parametrize("nk", [(256, 384), (128, 128)])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_grouped_mm_tall_tiles_ragged(fmt, transpose, nk):
+    """Enough tokens per expert for 256-row token tiles (T >= 256 E): groups
+    that end inside a tile, an empty expert and trailing rows in no group,
+    every output compared.  (128, 128) is the shortest reduction (two steps
+    of 64), (256, 384) runs the reduction loop in both directions."""
+    N, K = nk
+    counts = [700, 0, 301]
+    E = len(counts)
+    T = sum(counts) + 11
+    assert T >= 256 * E
+    say("tall", fmt, "transpose" if transpose else "forward", E, N, K, T)
+    q, wd = _weights(fmt, E, N, K, seed=39)
+    x = torch.randn(T, N if transpose else K, generator=torch.Generator().manual_seed(40)).to(torch.bfloat16)
+    offs = _offs(counts)
+    sentinel = torch.full((T, K if transpose else N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = _run(fmt, q, x, offs, transpose, sentinel)
+    ref, absref = oracle.grouped_mm(x, wd, offs, transpose)
+    T0 = sum(counts)
+    _check(y[:T0], ref[:T0], absref[:T0], N if transpose else K, f"tall {fmt}")
+    assert torch.isnan(y[T0:].float()).all(), "rows outside every group were written"
+
+
+@pytest.mark.parametrize("counts", [[512, 300], [100, 50]])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_grouped_mm_nan_scales(fmt, transpose, counts):
+    """NaN scale bytes (e8m0 0xFF; e4m3 0x7F and 0xFF) make their block's
+    weights NaN, and every output those weights reach is NaN: the GEMM's NaN
+    outputs are exactly the oracle's, the others within the bound.  Both
+    token-tile heights (256 rows for the first group mix, 128 for the
+    second)."""
+    E, N, K = 2, 256, 256
+    say("nan scales", fmt, "transpose" if transpose else "forward", counts)
+    q, _ = _weights(fmt, E, N, K, seed=41)
+    s = q[1].clone()
+    s[0, 3, 1] = 0xFF if fmt == "mxfp4" else 0x7F
+    s[1, 200, 0] = 0xFF
+    if fmt == "mxfp4":
+        q = (q[0], s)
+        wd = oracle.dequantize_mxfp4(q[0], s, torch.bfloat16)
+    else:
+        q = (q[0], s, q[2])
+        wd = oracle.dequantize_nvfp4(q[0], s, q[2], torch.bfloat16)
+    assert torch.isnan(wd.float()).any()
+    T = sum(counts)
+    x = torch.randn(T, N if transpose else K, generator=torch.Generator().manual_seed(42)).to(torch.bfloat16)
+    offs = _offs(counts)
+    y = _run(fmt, q, x, offs, transpose, torch.empty(T, K if transpose else N, dtype=torch.bfloat16, device=DEV))
+    ref, absref = oracle.grouped_mm(x, wd, offs, transpose)
+    nan_ref = torch.isnan(ref)
+    assert nan_ref.any() and not nan_ref.all()
+    assert torch.equal(torch.isnan(y.float()), nan_ref), "NaN outputs differ"
+    keep = ~nan_ref
+    _check(torch.where(keep, y, torch.zeros_like(y)), torch.where(keep, ref, torch.zeros_like(ref)),
+           torch.where(keep, absref, torch.zeros_like(absref)), N if transpose else K, f"nan {fmt}")
