@@ -56,18 +56,6 @@ struct Args {
   int64_t T, E, N, K;
 };
 
-// float32 value of an e4m3fn byte: the magnitude through the hardware e4m3
-// converter (exact for every finite byte; NaN for the NaN byte 0x7F), the
-// sign set by hand (so that 0x80 is -0).  Finite bytes decode bit for bit as
-// e4m3_decode_any does; a NaN byte gives the hardware's NaN, and every output
-// the weights of its block reach is NaN whatever the payload.  Four
-// instructions and no case split (the software decode's conditionals compile
-// to branches).
-__device__ __forceinline__ float e4m3_decode_hw(uint32_t b) {
-  const uint32_t d = fbits(__builtin_amdgcn_cvt_f32_fp8((int)(b & 0x7Fu), 0));
-  return bitsf(d | ((b & 0x80u) << 24));
-}
-
 // Dequantized bf16 of 8 consecutive weights (one packed dword) in the
 // arithmetic of dequantize_mxfp4 / dequantize_nvfp4 with a bf16 output, up
 // to the sign of zero: code 8 stays -0 here (the dequantizers give +0).  The

@@ -64,6 +64,21 @@ __device__ __forceinline__ void stream_st(T v, T* p) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// float32 value of an e4m3fn byte, branch-free: the hardware e4m3 converter
+// on the magnitude (exact for every finite byte; NaN for 0x7F) and the sign
+// set by hand, so that 0x80 is -0.  Finite bytes decode bit for bit as
+// e4m3_decode_any does; a NaN byte gives the hardware's NaN, which every
+// product with it propagates whatever the payload.  For code that must stay
+// one basic block (the GEMM's dequantization between its MFMAs): the case
+// split of e4m3_decode_any compiles to divergent branches, which there cost
+// 17% of the NVFP4 GEMM, while in the memory-bound dequantizers the branches
+// (skipped whole by waves without NaN or subnormal scales) are cheaper than
+// the converter.
+__device__ __forceinline__ float e4m3_decode_hw(uint32_t b) {
+  const uint32_t d = fbits(__builtin_amdgcn_cvt_f32_fp8((int)(b & 0x7Fu), 0));
+  return bitsf(d | ((b & 0x80u) << 24));
+}
+
 // ------------------------------------------------------------------ chunks
 // A "chunk" is 8 consecutive elements.  16-bit inputs move one 16-byte vector
 // per chunk, float32 inputs two.  Chunk c of a tensor starts at element 8c;
