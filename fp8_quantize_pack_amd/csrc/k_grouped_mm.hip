@@ -146,13 +146,16 @@ template <int FMT, int TRANS, int BM>
 __device__ __forceinline__ void load_stage(const Args& a, Stage<BM>& st, int tid, int64_t e,
                                            int64_t m0, int64_t m1, int64_t c0, int64_t r0,
                                            int64_t R) {
-  // activations: BM rows x 64 columns = 8 * BM chunks of 8, BM / 32 per thread
+  // activations: BM rows x 64 columns = 8 * BM chunks of 8, BM / 32 per thread.
+  // Rows past the end of the group read the group's last row instead (in
+  // bounds, and no branch around each load): they feed only accumulator rows
+  // that are never stored.
 #pragma unroll
   for (int i = 0; i < BM / 32; ++i) {
     const int c = tid + THREADS * i;
-    const int64_t row = m0 + (c >> 3);
-    st.av[i] = row < m1 ? *reinterpret_cast<const u32x4*>(a.x + row * R + r0 + (c & 7) * 8)
-                        : u32x4{0u, 0u, 0u, 0u};
+    int64_t row = m0 + (c >> 3);
+    row = row < m1 ? row : m1 - 1;
+    st.av[i] = *reinterpret_cast<const u32x4*>(a.x + row * R + r0 + (c & 7) * 8);
   }
   load_w<FMT, TRANS>(a, st.w, tid, e, c0, r0);
 }
