@@ -154,7 +154,7 @@ __device__ __forceinline__ void st1(void* p, int64_t i, float v) {
   } else if constexpr (DT == DT_BF16) {
     reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16_rne(v);
   } else {
-    reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_f16_rne(v);
+    reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)(f16x2_rne(v, 0.0f) & 0xFFFFu);
   }
 }
 

@@ -134,7 +134,7 @@ __device__ __forceinline__ float group_sum(float x) {
 template <int DT>
 __device__ __forceinline__ float round_to_dt(float v) {
   if constexpr (DT == DT_BF16) return bitsf(bf16x2_rne(v, 0.0f) << 16);
-  else if constexpr (DT == DT_F16) return f16_to_f32(f32_to_f16_rne(v));
+  else if constexpr (DT == DT_F16) return f16_to_f32(f16x2_rne(v, 0.0f) & 0xFFFFu);
   else return v;
 }
 

@@ -312,14 +312,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant_flat(
     for (int u = 0; u < kDqFlatUnroll; ++u) {
       const int64_t c = c0 + u * kWave;
       float f[8];
-      if constexpr (DT == DT_F16) {
-        nvfp4_dequant8(w[u], sb[u], g[u], f);
-      } else {
-        const float sigma = e4m3_decode_any(sb[u]);
-        e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
+      const float sigma = e4m3_decode_any(sb[u]);
+      e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g[u];     // exact, then RN
-      }
+      for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g[u];     // exact, then RN
       if (c < geo.nchunks) st8<DT>(y, c, f);
     }
   }
@@ -360,14 +356,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant_seg(
     for (int u = 0; u < kDqSegUnroll; ++u) {
       const int64_t j = seg * kDqSegChunks + u * kWave + lane;
       float f[8];
-      if constexpr (DT == DT_F16) {
-        nvfp4_dequant8(w[u], sb[u], g, f);
-      } else {
-        const float sigma = e4m3_decode_any(sb[u]);
-        e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
+      const float sigma = e4m3_decode_any(sb[u]);
+      e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g;        // exact, then RN
-      }
+      for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g;        // exact, then RN
       if (j < cpr) st8<DT>(y, rbase + j, f);
     }
   }

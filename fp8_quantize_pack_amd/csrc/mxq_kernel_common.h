@@ -163,14 +163,13 @@ __device__ __forceinline__ void st8<DT_BF16>(void* base, int64_t c, const float 
                                     bf16x2_rne(f[4], f[5]), bf16x2_rne(f[6], f[7])},
                               reinterpret_cast<u32x4*>(base) + c);
 }
+__device__ __forceinline__ uint32_t f16x2_rne(float lo, float hi);
+
 template <>
 __device__ __forceinline__ void st8<DT_F16>(void* base, int64_t c, const float f[8]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = f32_to_f16_rne(f[2 * i]) | (f32_to_f16_rne(f[2 * i + 1]) << 16);
-  stream_st(u32x4{w[0], w[1], w[2], w[3]},
-                              reinterpret_cast<u32x4*>(base) + c);
+  stream_st(u32x4{f16x2_rne(f[0], f[1]), f16x2_rne(f[2], f[3]),
+                  f16x2_rne(f[4], f[5]), f16x2_rne(f[6], f[7])},
+            reinterpret_cast<u32x4*>(base) + c);
 }
 
 // ------------------------------------------------------------------ gfx950 converts
@@ -298,6 +297,18 @@ __device__ __forceinline__ u32x4 e2m1_unpack8_bf16_hw(uint32_t w, float scale) {
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2v));
+}
+
+// Two float32 -> packed float16 pair, round to nearest even, IEEE overflow to
+// infinity, subnormals kept (v_cvt_pk_f16_f32 in the default float mode):
+// the same values as f32_to_f16_rne, a NaN staying a quiet NaN.  The empty
+// asm hands the conversion finished float32 values: it keeps the compiler
+// from fusing it with the product that made them into one mixed-precision
+// multiply-add, which would round once instead of twice and turn -0 into +0.
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f16x2_rne(float lo, float hi) {
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2v));
 }
 
 // ------------------------------------------------------------------ reductions
