@@ -562,10 +562,11 @@ def extra_ops(torch, mxq, synth, dev, x, y, reps):
     `reps` launches on resident inputs, with its algorithmic bytes (inputs
     read once, outputs written once) and its fraction of the HBM peak; not
     part of `value`.
-      * MXFP8 quantize / dequantize, the static two-level FP4 round trip
-        (block 16, calibrated block amax) and per-tensor NVFP4 quantize (a
-        whole-tensor amax pass, then the quantize pass) on one 36-expert
-        chunk of the sweep, bf16 [36, 2048, 7168];
+      * MXFP8 quantize / dequantize, MXFP4 and NVFP4 dequantize to
+        float16, the static two-level FP4 round trip (block 16, calibrated
+        block amax) and per-tensor NVFP4 quantize (a whole-tensor amax pass,
+        then the quantize pass) on one 36-expert chunk of the sweep, bf16
+        [36, 2048, 7168];
       * the NVFP4 KV cache: per-head quantization with k_smooth of K
         [32768, 12, 128] bf16 (two kernels: the per-head amax pass and the
         quantize pass; its bytes count K read once), and the paged
@@ -590,6 +591,22 @@ def extra_ops(torch, mxq, synth, dev, x, y, reps):
     record("mxfp8_dequant", b8, _time_launches(torch, lambda: mxq.mxq_dequantize_mxfp8(codes, sc8, ys), reps),
            shape=list(xs.shape))
     del codes, sc8
+    # float16 outputs of the two fp4 dequantizers on the same chunk (the
+    # sweep times the bf16 outputs)
+    rows_c = n // K
+    yh = torch.empty(xs.shape, dtype=torch.float16, device=dev)
+    pk = torch.empty((*xs.shape[:-1], K // 2), dtype=torch.uint8, device=dev)
+    sm = torch.empty((*xs.shape[:-1], K // 32), dtype=torch.uint8, device=dev)
+    mxq.mxq_quantize_mxfp4(xs, pk, sm)
+    record("mxfp4_dequant_f16", bytes_mx(n),
+           _time_launches(torch, lambda: mxq.mxq_dequantize_mxfp4(pk, sm, yh), reps), shape=list(xs.shape))
+    del sm
+    sn = torch.empty((*xs.shape[:-1], K // 16), dtype=torch.uint8, device=dev)
+    gn = torch.empty(xs.shape[:-1], dtype=torch.float32, device=dev)
+    mxq.mxq_quantize_nvfp4(xs, pk, sn, gn)
+    record("nvfp4_dequant_f16", bytes_nv(n, rows_c),
+           _time_launches(torch, lambda: mxq.mxq_dequantize_nvfp4(pk, sn, gn, yh), reps), shape=list(xs.shape))
+    del yh, pk, sn, gn
     amax = xs.abs().reshape(-1, K // 16, 16).amax(-1).float()    # calibrated block amax
     gam = xs.abs().max().float().reshape(1)
     bst = 2 * n + 2 * n + 4 * (n // 16) + 4

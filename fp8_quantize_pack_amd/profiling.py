@@ -33,7 +33,7 @@ from collections import defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # bench.py operation -> kernel (bfloat16 instantiations of the launched
-# templates for the shapes bench.py runs)
+# templates for the shapes bench.py runs, float16 where the op says so)
 BENCH_KERNELS = {
     "mxfp4_quant": "mxq::k_mxfp4_quant<1>",
     "mxfp4_dequant": "mxq::k_mxfp4_dequant<1>",
@@ -46,6 +46,8 @@ BENCH_KERNELS = {
     "nvfp4_quant_tensor_mode": "mxq::k_nvfp4_quant_seg<1, 4, 1, true>",
     "mxfp8_quant": "mxq::k_mxfp8_quant<1>",
     "mxfp8_dequant": "mxq::k_mxfp8_dequant<1>",
+    "mxfp4_dequant_f16": "mxq::k_mxfp4_dequant<2>",
+    "nvfp4_dequant_f16": "mxq::k_nvfp4_dequant_seg<2>",
     "fp4_static_qdq": "mxq::k_fp4_static_qdq<1>",
     "kv_head_amax": "mxq::k_kv_head_amax<1, true, 16>",
     "kv_quant": "mxq::k_kv_quant<1, true, 16>",
