@@ -281,7 +281,8 @@ def main():
 
     gemm = None if args.no_gemm else grouped_gemm(torch, mxq, dev, max(args.steps, 1))
     progress("grouped GEMM measured" if gemm else "grouped GEMM skipped")
-    extra = None if args.no_extra else extra_ops(torch, mxq, synth, dev, x, y, max(args.steps, 1))
+    extra = None if args.no_extra else extra_ops(torch, mxq, synth, dev, x, y, max(args.steps, 1),
+                                                 (mx_p, mx_s, nv_p, nv_s, nv_g))
     progress("extra ops measured" if extra else "extra ops skipped")
 
     if args.calibrate_copy:
@@ -557,7 +558,7 @@ def _time_launches(torch, fn, reps):
     return a.elapsed_time(b) / reps * 1e-3
 
 
-def extra_ops(torch, mxq, synth, dev, x, y, reps):
+def extra_ops(torch, mxq, synth, dev, x, y, reps, sweep_codes):
     """The other calls of the library, each timed with HIP events around
     `reps` launches on resident inputs, with its algorithmic bytes (inputs
     read once, outputs written once) and its fraction of the HBM peak; not
@@ -591,22 +592,15 @@ def extra_ops(torch, mxq, synth, dev, x, y, reps):
     record("mxfp8_dequant", b8, _time_launches(torch, lambda: mxq.mxq_dequantize_mxfp8(codes, sc8, ys), reps),
            shape=list(xs.shape))
     del codes, sc8
-    # float16 outputs of the two fp4 dequantizers on the same chunk (the
-    # sweep times the bf16 outputs)
-    rows_c = n // K
+    # float16 outputs of the two fp4 dequantizers on the same chunk, from the
+    # codes the sweep left for it (the sweep times the bf16 outputs)
+    mp, ms, np_, ns, ng = (t[:ne] for t in sweep_codes)
     yh = torch.empty(xs.shape, dtype=torch.float16, device=dev)
-    pk = torch.empty((*xs.shape[:-1], K // 2), dtype=torch.uint8, device=dev)
-    sm = torch.empty((*xs.shape[:-1], K // 32), dtype=torch.uint8, device=dev)
-    mxq.mxq_quantize_mxfp4(xs, pk, sm)
     record("mxfp4_dequant_f16", bytes_mx(n),
-           _time_launches(torch, lambda: mxq.mxq_dequantize_mxfp4(pk, sm, yh), reps), shape=list(xs.shape))
-    del sm
-    sn = torch.empty((*xs.shape[:-1], K // 16), dtype=torch.uint8, device=dev)
-    gn = torch.empty(xs.shape[:-1], dtype=torch.float32, device=dev)
-    mxq.mxq_quantize_nvfp4(xs, pk, sn, gn)
-    record("nvfp4_dequant_f16", bytes_nv(n, rows_c),
-           _time_launches(torch, lambda: mxq.mxq_dequantize_nvfp4(pk, sn, gn, yh), reps), shape=list(xs.shape))
-    del yh, pk, sn, gn
+           _time_launches(torch, lambda: mxq.mxq_dequantize_mxfp4(mp, ms, yh), reps), shape=list(xs.shape))
+    record("nvfp4_dequant_f16", bytes_nv(n, n // K),
+           _time_launches(torch, lambda: mxq.mxq_dequantize_nvfp4(np_, ns, ng, yh), reps), shape=list(xs.shape))
+    del yh
     amax = xs.abs().reshape(-1, K // 16, 16).amax(-1).float()    # calibrated block amax
     gam = xs.abs().max().float().reshape(1)
     bst = 2 * n + 2 * n + 4 * (n // 16) + 4
