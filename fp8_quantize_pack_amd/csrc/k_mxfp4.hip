@@ -135,27 +135,23 @@ __global__ __launch_bounds__(64 * kMxWaves) void k_mxfp4_dequant(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t c = c0 + u * kWave;
-      if constexpr (DT == DT_F16) {
-        float f[8];
-        mxfp4_dequant8(w[u], sb[u], f);
-        if (c < nchunks) st8<DT>(y, c, f);
+      const uint32_t wc = e2m1_canonical_zeros(w[u]);
+      const float scale = e8m0_as_scale(sb[u]);
+      const bool nan_scale = sb[u] == 255u;               // e8m0 NaN
+      if constexpr (DT == DT_BF16) {
+        u32x4 o = e2m1_unpack8_bf16_hw(wc, scale);
+        if (nan_scale) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+        if (c < nchunks) stream_st(o, reinterpret_cast<u32x4*>(y) + c);
       } else {
-        const uint32_t wc = e2m1_canonical_zeros(w[u]);
-        const float scale = e8m0_as_scale(sb[u]);
-        const bool nan_scale = sb[u] == 255u;             // e8m0 NaN
-        if constexpr (DT == DT_BF16) {
-          u32x4 o = e2m1_unpack8_bf16_hw(wc, scale);
-          if (nan_scale) o = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
-          if (c < nchunks) stream_st(o, reinterpret_cast<u32x4*>(y) + c);
-        } else {
-          float f[8];
-          e2m1_unpack8_f32_hw(wc, scale, f);
-          if (nan_scale) {
+        // float32 (exact: a code times a power of two), then for float16 one
+        // rounding to nearest even in st8
+        float f[8];
+        e2m1_unpack8_f32_hw(wc, scale, f);
+        if (nan_scale) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) f[i] = bitsf(0x7FC00000u);
-          }
-          if (c < nchunks) st8<DT>(y, c, f);
+          for (int i = 0; i < 8; ++i) f[i] = bitsf(0x7FC00000u);
         }
+        if (c < nchunks) st8<DT>(y, c, f);
       }
     }
   }
