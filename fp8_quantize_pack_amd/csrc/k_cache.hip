@@ -52,7 +52,7 @@ __device__ __forceinline__ void cache_chunk(const Raw8<DT>& raw, bool ok, void* 
   a = group_max<G>(a);
   const CacheGroupScale gs = cache_scale(FMT, a);
   float o[8];
-  if constexpr (FMT == FMT_FP8 || DT == DT_F16) {
+  if constexpr (FMT == FMT_FP8) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = cache_qdq1(FMT, DT == DT_F32, f[i], gs);
   } else {

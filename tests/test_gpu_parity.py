@@ -470,6 +470,20 @@ def test_cache_all_bf16_values(fmt):
         assert_same(gpu_quantize_cache(v.to(DEV), fmt, B), oracle.quantize_cache(v, fmt, B), f"B={B}")
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "nvfp4"])
+def test_cache_all_f16_values(fmt):
+    """Every finite float16 value (subnormals, both zeros, the largest
+    magnitudes) in shuffled groups of 32 and 16 through the cache round trip
+    with float16 in and out."""
+    say("cache all f16 values", fmt)
+    v = torch.from_numpy(np.arange(1 << 16, dtype=np.uint16).view(np.float16).copy())
+    v = v[torch.isfinite(v)]
+    v = v[torch.randperm(v.numel(), generator=torch.Generator().manual_seed(4))]
+    v = torch.nn.functional.pad(v, (0, (-v.numel()) % 32)).reshape(-1, 32)
+    for B in (32, 16):
+        assert_same(gpu_quantize_cache(v.to(DEV), fmt, B), oracle.quantize_cache(v, fmt, B), f"B={B}")
+
+
 # ------------------------------------------------------------------ full-size workloads (whole tensors)
 #
 # Every full-size workload is compared whole: every packed byte, scale byte,
