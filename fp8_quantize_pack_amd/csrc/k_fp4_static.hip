@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64 * kStWaves) void k_fp4_static_qdq(
       e2m1_unpack8_f32_hw(w, 1.0f, o);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = o[i] * sp;   // one float32 rounding
-      if (c < nchunks) st8<DT>(y, c, o);
+      st8_wave<DT>(y, c - lane, nchunks, lane, o);
     }
   }
 }

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void k_kv_pages_dequant(
       e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g;   // left to right, float32
-      if (c < cpb) st8<DT>(y, b * cpb + c, f);
+      st8_wave<DT>(y, b * cpb + c - lane, b * cpb + cpb, lane, f);
     }
   }
 }

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(64 * kMxWaves) void k_mxfp4_dequant(
 #pragma unroll
           for (int i = 0; i < 8; ++i) f[i] = bitsf(0x7FC00000u);
         }
-        if (c < nchunks) st8<DT>(y, c, f);
+        st8_wave<DT>(y, c - lane, nchunks, lane, f);
       }
     }
   }

@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant_flat(
       e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g[u];     // exact, then RN
-      if (c < geo.nchunks) st8<DT>(y, c, f);
+      st8_wave<DT>(y, c - lane, geo.nchunks, lane, f);
     }
   }
 }
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant_seg(
       e2m1_unpack8_f32_hw(e2m1_canonical_zeros(w[u]), 1.0f, f);   // exact e2m1
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = (f[i] * sigma) * g;        // exact, then RN
-      if (j < cpr) st8<DT>(y, rbase + j, f);
+      st8_wave<DT>(y, rbase + j - lane, rbase + cpr, lane, f);
     }
   }
 }
