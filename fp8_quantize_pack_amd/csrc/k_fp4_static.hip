@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * kStWaves) void k_fp4_static_qdq(
     for (int u = 0; u < kStUnroll; ++u) {
       const int64_t c = c0 + u * kWave;
       const bool ok = c < nchunks;
-      r[u] = ok ? ld8<DT>(x, c) : zero8<DT>();
+      r[u] = ld8_wave<DT>(x, c - lane, nchunks, lane);
       a[u] = ok ? block_amax[c >> cpb_log2] : 0.0f;
     }
 #pragma unroll

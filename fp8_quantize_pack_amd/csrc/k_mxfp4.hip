@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64 * kMxWaves) void k_mxfp4_quant(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t c = c0 + u * kWave;
-      r[u] = (c < nchunks) ? ld8<DT>(x, c) : zero8<DT>();
+      r[u] = ld8_wave<DT>(x, c - lane, nchunks, lane);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {

@@ -172,6 +172,38 @@ __device__ __forceinline__ void st8<DT_F16>(void* base, int64_t c, const float f
             reinterpret_cast<u32x4*>(base) + c);
 }
 
+// Load chunk cw + l into lane l of a wave (cw uniform over the wave; zeros at
+// or past `end`).  Every lane of the wave must call this together.  For
+// float32 the two load instructions read one contiguous 1 KiB each (chunks
+// cw .. cw + 31, then cw + 32 .. cw + 63; lane l: half l % 2 of chunk l / 2)
+// and the lanes trade halves through ds_bpermute, instead of each
+// instruction reading every other 16 bytes of the wave's 2 KiB.  16-bit
+// inputs load per lane, as ld8 does.
+template <int DT>
+__device__ __forceinline__ Raw8<DT> ld8_wave(const void* base, int64_t cw, int64_t end, int lane) {
+  if constexpr (DT != DT_F32) {
+    return (cw + lane < end) ? ld8<DT>(base, cw + lane) : zero8<DT>();
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(base) + 2 * cw;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 a = (cw + (lane >> 1) < end) ? stream_ld(p + lane) : z;
+    const u32x4 b = (cw + 32 + (lane >> 1) < end) ? stream_ld(p + 64 + lane) : z;
+    // chunk cw + lane: its halves sit at positions 2 lane and 2 lane + 1 of
+    // (a of lanes 0..63, then b of lanes 0..63)
+    const int s0 = ((2 * lane) & 63) << 2, s1 = ((2 * lane + 1) & 63) << 2;
+    const bool from_a = lane < 32;
+    auto pull = [&](int src, uint32_t av, uint32_t bv) -> uint32_t {
+      const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)av);
+      const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)bv);
+      return from_a ? x : y;
+    };
+    Raw8<DT_F32> r;
+    r.a = u32x4{pull(s0, a.x, b.x), pull(s0, a.y, b.y), pull(s0, a.z, b.z), pull(s0, a.w, b.w)};
+    r.b = u32x4{pull(s1, a.x, b.x), pull(s1, a.y, b.y), pull(s1, a.z, b.z), pull(s1, a.w, b.w)};
+    return r;
+  }
+}
+
 // Store the 8 results of every lane of a wave whose lane l holds chunk
 // cw + l (cw uniform over the wave); chunks at or past `end` are not stored.
 // Every lane of the wave must call this together.  A float32 chunk is 32
