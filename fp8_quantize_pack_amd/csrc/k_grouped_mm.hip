@@ -345,12 +345,13 @@ void k_grouped_mm(Args a, int64_t ntiles_c) {
     // strategy 0) measured 2-2.5% faster for NVFP4 both ways (forward 536 ->
     // 526 us, backward 551 -> 538 us on the expert shapes) and for the MXFP4
     // forward (296 -> 289 us); the MXFP4 backward moved within run-to-run
-    // noise (+-2%), so it keeps the compiler's own schedule.
+    // noise (+-2%), so it keeps the compiler's own schedule.  With the
+    // branch-free NVFP4 decode, no hint or strategy 1 was 4-7% slower.
     else if constexpr (BM == 256 && !MXQ_GMM_IGLP_256 && (FMT != FMT_MXFP4 || TRANS == 0))
       __builtin_amdgcn_iglp_opt(0);
     // MXFP4: waves in their MFMA phase take issue priority over those loading,
     // dequantizing and storing the next tile (2.5-4% faster both ways); NVFP4's
-    // heavier dequantization needs the issue slots (3% slower backward)
+    // heavier dequantization needs the issue slots (3% slower both ways)
     if constexpr (FMT == FMT_MXFP4 && (BM == 128 || MXQ_GMM_PRIO_256)) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
