@@ -14,9 +14,10 @@
 // tokens b * block_tokens .. of the output [blocks * block_tokens, H, D], so
 // the output is the blocks' rows concatenated.  Each wavefront owns a tile of
 // 8 x 64 consecutive 8-element chunks of one block: it reads the block's
-// pointers and amax once (uniform), then per step a packed dword and a scale
-// byte per lane, and writes 16 bytes (bfloat16) per lane, contiguous over the
-// wave.
+// pointers and amax once (uniform) and the tile's scale bytes as one dword
+// per lane, then per step a packed dword per lane (and its scale byte from
+// another lane's dword), and writes 16 bytes (bfloat16) per lane, contiguous
+// over the wave.
 //
 // Quantization with k_smooth.  k [S, H, D], D a power of two in [16, 512].
 // Each row (token, head) of D values is optionally smoothed: its mean is the
@@ -72,12 +73,28 @@ __global__ __launch_bounds__(256) void k_kv_pages_dequant(
     const GlobalU8* sb = (const GlobalU8*)(scales[b]);
     const float g = *(const GlobalF32*)(amax[b]) / kGlobalDiv;
     uint32_t w[kKvUnroll], s[kKvUnroll];
+    // A whole tile's 256 scale bytes are contiguous (16-byte aligned): lane l
+    // loads dword l and step u takes the byte of chunk c0 + 64 u -- byte
+    // 32 u + l / 2, in dword 8 u + l / 8 -- by a lane permute instead of a
+    // byte load of its own.  A partial last tile loads bytes.
+    static_assert(kKvUnroll == 8, "one scale dword per lane covers the tile");
+    const bool full = c0 - lane + kKvTileChunks <= cpb;   // uniform over the wave
+    if (full) {
+      const uint32_t sd = __builtin_nontemporal_load((const GlobalU32*)(sb + ((c0 - lane) >> 1)) + lane);
+      const int sh = 8 * ((lane >> 1) & 3);
 #pragma unroll
-    for (int u = 0; u < kKvUnroll; ++u) {
-      const int64_t c = c0 + u * kWave;
-      const bool ok = c < cpb;
-      w[u] = ok ? __builtin_nontemporal_load(vb + c) : 0u;
-      s[u] = ok ? (uint32_t)sb[c >> 1] : 0u;
+      for (int u = 0; u < kKvUnroll; ++u) {
+        w[u] = __builtin_nontemporal_load(vb + c0 + u * kWave);
+        s[u] = ((uint32_t)__builtin_amdgcn_ds_bpermute(4 * (8 * u + (lane >> 3)), (int)sd) >> sh) & 0xFFu;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kKvUnroll; ++u) {
+        const int64_t c = c0 + u * kWave;
+        const bool ok = c < cpb;
+        w[u] = ok ? __builtin_nontemporal_load(vb + c) : 0u;
+        s[u] = ok ? (uint32_t)sb[c >> 1] : 0u;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kKvUnroll; ++u) {
