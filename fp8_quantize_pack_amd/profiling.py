@@ -52,10 +52,10 @@ BENCH_KERNELS = {
     "kv_head_amax": "mxq::k_kv_head_amax<1, true, 16>",
     "kv_quant": "mxq::k_kv_quant<1, true, 16>",
     "kv_pages_dequant": "mxq::k_kv_pages_dequant<1>",
-    "gemm_mxfp4_forward": "mxq::gmm::k_grouped_mm<1, 0, 256>",
-    "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1, 256>",
-    "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0, 256>",
-    "gemm_nvfp4_backward": "mxq::gmm::k_grouped_mm<2, 1, 256>",
+    "gemm_mxfp4_forward": "mxq::gmm::k_grouped_mm<1, 0, 256, true>",
+    "gemm_mxfp4_backward": "mxq::gmm::k_grouped_mm<1, 1, 256, true>",
+    "gemm_nvfp4_forward": "mxq::gmm::k_grouped_mm<2, 0, 256, false>",
+    "gemm_nvfp4_backward": "mxq::gmm::k_grouped_mm<2, 1, 256, false>",
     "ref_copy_u1": "(anonymous namespace)::k_copy<1>",
     "ref_copy_u2": "(anonymous namespace)::k_copy<2>",
     "ref_copy_u4": "(anonymous namespace)::k_copy<4>",
