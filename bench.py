@@ -497,7 +497,8 @@ def grouped_gemm(torch, mxq, dev, reps):
                 fn = lambda: mxq.mxq_grouped_mm_mxfp4(x, packed.view(torch.int8), scales, offs, y, tr)
             else:
                 fn = lambda: mxq.mxq_grouped_mm_nvfp4(x, packed, scales, rs, offs, y, tr)
-            fn()
+            for _ in range(GEMM_WARMUP):
+                fn()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -510,7 +511,8 @@ def grouped_gemm(torch, mxq, dev, reps):
             # dense reference: [E, per, R] @ [E, R, C], both contiguous
             xd = x.view(E, per, N if tr else K)
             wd = torch.randn(E, N if tr else K, K if tr else N, device=dev, generator=g).to(torch.bfloat16)
-            yd = torch.bmm(xd, wd)
+            for _ in range(GEMM_WARMUP):
+                yd = torch.bmm(xd, wd)
             torch.cuda.synchronize()
             a.record()
             for _ in range(reps):
@@ -528,7 +530,11 @@ def grouped_gemm(torch, mxq, dev, reps):
                 deq = lambda: mxq.mxq_dequantize_nvfp4(packed, scales, rs, wq)
             wr = wq if tr else wq.view(E, K, N)
             comp = lambda: (deq(), torch.bmm(xd, wr, out=yd))
+            for _ in range(GEMM_WARMUP - 1):      # _time_launches adds one more
+                deq()
             t_deq = _time_launches(torch, deq, reps)
+            for _ in range(GEMM_WARMUP - 1):
+                comp()
             t_comp = _time_launches(torch, comp, reps)
             del wq, wr, yd
             out[f"{fmt}_{'backward' if tr else 'forward'}"] = {
@@ -544,6 +550,9 @@ def grouped_gemm(torch, mxq, dev, reps):
 
 
 KV_SETS = 8
+# launches of each product before its timed burst: the first launches after
+# other work run at a lower clock (up to 20% slower in a burst of GEMMs)
+GEMM_WARMUP = 3
 
 
 def _time_launches(torch, fn, reps):
