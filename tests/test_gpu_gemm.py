@@ -231,6 +231,35 @@ def test_grouped_mm_tall_tiles_ragged(fmt, transpose, nk):
     assert torch.isnan(y[T0:].float()).all(), "rows outside every group were written"
 
 
+# ------------------------------------------------------------------ a reduction of 2^22
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_grouped_mm_mxfp4_long_reduction(transpose):
+    """A reduction of 2^22 values (the forward's K, the backward's N): a
+    token tile would need byte offsets of 2^31 or more from its first row, so
+    the MXFP4 activations take the 64-bit pointer path instead of the buffer
+    resource that every shorter MXFP4 shape here uses.  One expert, three
+    tokens; random codes and scale bytes, dequantized by the oracle.  The
+    backward reference is the oracle's forward sum over the transposed
+    weights (the same products; the oracle reads its weights contiguously
+    that way)."""
+    R, C, T = 1 << 22, 128, 3
+    N, K = (R, C) if transpose else (C, R)
+    g = torch.Generator().manual_seed(41)
+    p = torch.randint(0, 256, (1, N, K // 2), dtype=torch.uint8, generator=g)
+    s = torch.randint(118, 126, (1, N, K // 32), dtype=torch.uint8, generator=g)
+    wd = oracle.dequantize_mxfp4(p.view(torch.int8), s, torch.bfloat16)
+    x = torch.randn(T, R, generator=g).to(torch.bfloat16)
+    offs = _offs([T])
+    say("mxfp4 long reduction", "transpose" if transpose else "forward", N, K, T)
+    y = _run("mxfp4", (p.view(torch.int8), s), x, offs, transpose,
+             torch.empty(T, C, dtype=torch.bfloat16, device=DEV))
+    w_fwd = wd.transpose(1, 2).contiguous() if transpose else wd      # [1, C, R]
+    del wd
+    ref, absref = oracle.grouped_mm(x, w_fwd, offs, False)
+    _check(y, ref, absref, R, "mxfp4 long reduction")
+
+
 @pytest.mark.parametrize("counts", [[512, 300], [100, 50]])
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("transpose", [False, True])
