@@ -21,10 +21,10 @@
 // down through a one-ulp step toward zero and round-to-nearest-even; float32
 // inputs and nvfp4 quotients rounded up to 22 significant bits first, which
 // changes no decision) and decode with the exact fp4 dequantizer;
-// the nvfp4 quotient x / sigma is taken as a binary64 product with the
-// correctly rounded 1 / sigma: x has at most 24 significant bits and sigma 4,
-// so x / sigma is never a float32 decision boundary and lies at least 2^-29
-// (relative) away from each, far beyond the product's 2^-52 error.
+// the nvfp4 quotient x / sigma is taken as a binary64 product with 1 / sigma
+// to about 2^-52: x has at most 24 significant bits and sigma 4, so x / sigma
+// is never a float32 decision boundary and lies at least 2^-29 (relative)
+// away from each, far beyond the product's error of about 2^-51.
 #include "mxq_kernel_common.h"
 #include "mxq_launch.h"
 
@@ -65,7 +65,10 @@ __device__ __forceinline__ void cache_chunk(const Raw8<DT>& raw, bool ok, void* 
       for (int i = 0; i < 8; ++i) q[i] = (DT == DT_F32) ? ceil22(f[i]) : f[i];
       cvt_scale = gs.s;                         // power of two: x / s inside
     } else {
-      const double rs = 1.0 / (double)gs.s;     // sigma: an e4m3 value
+      // sigma: an e4m3 value in [2^-9, 448]; 1 / sigma to about 2^-52
+      // (hardware reciprocal and two Newton steps), far inside the 2^-29
+      // margin of the quotient (see the header)
+      const double rs = recip64((double)gs.s);
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = half_down_for_rne((float)((double)f[i] * rs));
       cvt_scale = 1.0f;

@@ -370,14 +370,27 @@ struct CacheGroupScale {
   float half_s;  // s / 2: twice-magnitude integers times this are e2m1 * s
 };
 
+// float32 round-to-nearest of a / 448 (a >= 0 finite) for quotients of at
+// least 2^-126, as a binary64 product with a correctly rounded 1/448 rounded
+// once to float32.  With a = M 2^E (M < 2^24), a / 448 = M 2^E / (7 2^6) is an
+// exact float32 value of at most 21 significant bits when 7 divides M, and
+// otherwise differs from every float32 rounding boundary (a 25-bit odd
+// multiple, B) by |M 2^E - 448 B| / 448 >= 2^(f-19) / 448 for a quotient in
+// [2^f, 2^(f+1)) (E > f - 16): at least 2^-27.8 relative, against the
+// product's 2^-52.  Below 2^-126 the results may differ, which the clamp to
+// 2^-126 in cache_scale hides (both sides then give 2^-126).
+MXQ_HD float div448_rn_normal(float a) { return (float)((double)a * (1.0 / 448.0)); }
+
 MXQ_HD CacheGroupScale cache_scale(int fmt, float a) {
   CacheGroupScale r;
   if (fmt == FMT_FP8 || fmt == FMT_MXFP4) {
-    const float v = fmaxf(a / (fmt == FMT_FP8 ? 448.0f : 6.0f), 1.17549435e-38f);
+    // a / 448 and a / 6 rounded to nearest, as binary64 products (3 VALU
+    // operations instead of a correctly rounded float32 division)
+    const float v = fmaxf(fmt == FMT_FP8 ? div448_rn_normal(a) : div6_rn(a), 1.17549435e-38f);
     r.s = pow2_ceil(v);
     r.inv = bitsf((254u - (fbits(r.s) >> 23)) << 23);   // 2^-k, exact
   } else {
-    const float u = fminf(fmaxf(a / 6.0f, 0.001953125f), 448.0f);
+    const float u = fminf(fmaxf(div6_rn(a), 0.001953125f), 448.0f);
     e4m3_encode_clamped(u, &r.s);
     r.inv = 0.0f;                                      // nvfp4 divides by s
   }

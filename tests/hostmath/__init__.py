@@ -45,6 +45,8 @@ def lib():
         L.hm_nv_division_stress.restype = i64
         L.hm_ceil22_check.argtypes = []
         L.hm_ceil22_check.restype = i64
+        L.hm_scale_division_check.argtypes = []
+        L.hm_scale_division_check.restype = i64
         L.hm_half_down_check.argtypes = []
         L.hm_half_down_check.restype = i64
         L.hm_rne_model_check.argtypes = []

@@ -242,3 +242,36 @@ extern "C" int64_t hm_ceil22_check(void) {
   if (e2m1_mag_f32(ceil22(bitsf(0x7F800000u))) != 7u) ++bad;
   return bad;
 }
+
+// Every non-negative finite float32 a: the cache scales' binary64-product
+// quotients against IEEE float32 division.  a / 6 (div6_rn) must be equal for
+// every a; a / 448 (div448_rn_normal) must be equal whenever the quotient is
+// at least 2^-126, and in every case after the clamp to 2^-126 that follows
+// it.  Returns the number of disagreements.
+static int64_t scale_division_range(uint32_t lo, uint32_t hi) {
+  int64_t bad = 0;
+  const float tiny = 1.17549435e-38f;
+  for (uint32_t b = lo; b < hi; ++b) {
+    const float a = bitsf(b);
+    if (fbits(div6_rn(a)) != fbits(a / 6.0f)) ++bad;
+    const float q = a / 448.0f, p = div448_rn_normal(a);
+    if (q >= tiny && fbits(p) != fbits(q)) ++bad;
+    if (fbits(fmaxf(p, tiny)) != fbits(fmaxf(q, tiny))) ++bad;
+  }
+  return bad;
+}
+
+extern "C" int64_t hm_scale_division_check(void) {
+  constexpr uint32_t kEnd = 0x7F800000u;       // every finite non-negative float32
+  constexpr int kParts = 8;
+  int64_t part[kParts] = {};
+  std::vector<std::thread> pool;
+  for (int t = 0; t < kParts; ++t)
+    pool.emplace_back([&part, t] {
+      part[t] = scale_division_range((uint32_t)((uint64_t)kEnd * t / kParts),
+                                     (uint32_t)((uint64_t)kEnd * (t + 1) / kParts));
+    });
+  int64_t bad = 0;
+  for (int t = 0; t < kParts; ++t) { pool[t].join(); bad += part[t]; }
+  return bad;
+}

@@ -256,6 +256,14 @@ def test_nvfp4_binary64_division_shortcut_stress(wide):
     assert hm.lib().hm_nv_division_stress(3_000_000, 1234 + wide, wide) == 0
 
 
+def test_cache_scale_binary64_quotients_exhaustive():
+    """The cache scales take a / 6 and a / 448 as binary64 products rounded
+    once to float32: over every non-negative finite float32 they equal IEEE
+    float32 division (a / 448 wherever the quotient is at least 2^-126, and
+    after the clamp to 2^-126 everywhere)."""
+    assert hm.lib().hm_scale_division_check() == 0
+
+
 def test_rounding_up_to_22_bits_keeps_every_e2m1_decision():
     """Exhaustive over all float32 magnitudes below 16 (about 1.1e9 values)."""
     assert hm.lib().hm_ceil22_check() == 0
